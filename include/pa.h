@@ -1,0 +1,188 @@
+/*
+ * pa.h -- PagedAttention over a block-paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * One serving step runs two calls on the caller's HIP stream:
+ *
+ *   1. pa_reshape_and_cache: write the step's new K/V rows into the block pool at the
+ *      slots given by a per-token slot mapping.
+ *   2. pa_attention: causal attention for every query row of the step. The rows come
+ *      from all scheduled sequences, flattened into one "super-sequence"; decode rows
+ *      and chunked-prefill rows are mixed freely. K/V are gathered through each
+ *      sequence's block table. Query heads share kv heads in contiguous groups (GQA).
+ *
+ * Sources (web pages that summarise the article "Inside vLLM: Anatomy of a
+ * High-Throughput LLM Inference System"):
+ *   - KV cache kept in fixed blocks that are handed out and reclaimed on demand:
+ *     chat-gpts.plus news summary, section 事件核心; 16 tokens per block by default:
+ *     shengyayun.com "读懂 vLLM 推理引擎内幕", section 关键实现细节, item 1.
+ *   - Positions and slot mapping are prepared for each step; all scheduled sequences
+ *     are flattened into one super-sequence for a custom paged-attention kernel:
+ *     hn.213312.xyz restatement "深入解析 vLLM", section 一, forward pass.
+ *   - Decode and prefill mixed in one step; long prompts cut into chunks:
+ *     same restatement, section 一 (scheduler) and section 二, item 1.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   BLOCK   = PA_BLOCK_SIZE = 16 tokens per block.
+ *   S       = num_seqs, T = num_tokens, Hq / Hkv = query / kv heads, G = Hq / Hkv,
+ *   D       = head_dim, NB = num_blocks, MB = max_blocks_per_seq.
+ *   Layouts (all row-major and contiguous; element strides are implied by the shapes):
+ *     q, out        [T, Hq, D]
+ *     k, v          [T, Hkv, D]            (new rows of this step)
+ *     k_cache       [NB, Hkv, BLOCK, D]    k_cache[b][h][o][d] = dim d of the key of the
+ *                                          token in slot BLOCK*b + o, kv head h
+ *     v_cache       [NB, Hkv, D, BLOCK]    v_cache[b][h][d][o] = dim d of that token's value
+ *     block_tables  [S, MB] int32          logical block j of sequence i lives in block
+ *                                          block_tables[i][j]; entries at or past
+ *                                          ceil(seq_lens[i] / BLOCK) are never read
+ *     seq_lens      [S] int32              tokens of sequence i after this step
+ *     context_lens  [S] int32              tokens of sequence i cached before this step
+ *     query_start_loc [S+1] int32          rows of sequence i are [qsl[i], qsl[i+1]);
+ *                                          qsl[0] = 0, non-decreasing, qsl[S] <= T
+ *     slot_mapping  [T] int64              slot = BLOCK * block + offset, or -1 = skip
+ *   Row r of sequence i is the token at position context_lens[i] + r; it sees keys
+ *   0 .. context_lens[i] + r of its sequence. Query head h reads kv head h / G.
+ *   Payload dtype is one of pa_dtype and is the same for q, k, v, both caches and out;
+ *   all accumulation is fp32.
+ *
+ * Ownership: every pointer is caller-owned device memory (except pa_*_size outputs,
+ * which are host pointers). The library keeps no pointer after a call returns and
+ * allocates no device memory in these calls. Device buffers must stay alive until
+ * the stream has passed the work.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; a non-OK
+ * status means nothing was enqueued, and pa_last_error() gives the detail (per host
+ * thread). Index values stored in device memory (block ids, slots, lengths) are not
+ * checked: breaking the preconditions below is undefined behaviour. No C++ exception
+ * crosses this interface.
+ *
+ * Preconditions: non-negative slots are pairwise distinct; seq_lens[i] =
+ * context_lens[i] + (qsl[i+1] - qsl[i]); every block id a sequence reads lies in
+ * [0, NB); out does not overlap q; k_cache does not overlap v_cache; payload
+ * pointers are 16-byte aligned.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+#define PA_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_E_NULL = 1,        /* a required pointer is NULL                                  */
+  PA_E_DTYPE = 2,       /* unknown payload dtype                                       */
+  PA_E_SHAPE = 3,       /* a size is negative, zero where it must not be, or too big   */
+  PA_E_UNSUPPORTED = 4, /* valid but not provided: head_dim not 64/128, G not in 1..16 */
+  PA_E_ALIGN = 5,       /* a payload pointer is not 16-byte aligned                    */
+  PA_E_WORKSPACE = 6,   /* workspace NULL or smaller than pa_attention_workspace_size  */
+  PA_E_HIP = 7          /* the HIP runtime reported an error (launch or event)        */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,  /* IEEE binary32                          */
+  PA_BF16 = 1  /* bfloat16 (upper half of a binary32)    */
+} pa_dtype;
+
+/* Constant string naming a status. Never NULL. */
+const char* pa_status_string(pa_status s);
+
+/* Detail of the last non-OK status returned on this host thread ("" if none). */
+const char* pa_last_error(void);
+
+/* PA_VERSION of the built library. */
+int pa_version(void);
+
+/*
+ * Positions and slot mapping of the step's tokens (the step's index preparation,
+ * restatement section 一, forward pass).
+ *   positions[t]    = context_lens[i] + (t - qsl[i])        for qsl[i] <= t < qsl[i+1]
+ *   slot_mapping[t] = block_tables[i][p / 16] * 16 + p % 16  with p = positions[t]
+ * Rows t >= qsl[S] (padding) get position 0 and slot -1.
+ * positions may be NULL (not written). block_tables is [S, MB] int32.
+ * Errors: PA_E_NULL, PA_E_SHAPE (negative sizes, MB < 1 with S > 0), PA_E_HIP.
+ */
+pa_status pa_build_slot_mapping(const int32_t* block_tables, const int32_t* query_start_loc,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_blocks_per_seq, int64_t num_tokens,
+                                int32_t* positions, int64_t* slot_mapping, void* stream);
+
+/*
+ * Cache write ("reshape_and_cache"): for every t < num_tokens with s = slot_mapping[t] >= 0,
+ *   k_cache[s/16][h][s%16][:] = k[t][h][:]   and   v_cache[s/16][h][:][s%16] = v[t][h][:]
+ * for all kv heads h. A bit copy: stored bits equal the input bits. Other slots are
+ * not touched. Slots must lie in [-1, 16*NB) and be distinct when non-negative.
+ * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED (D not 64/128),
+ * PA_E_ALIGN, PA_E_HIP.
+ */
+pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int64_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                               pa_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace pa_attention needs for these sizes (written to *bytes).
+ * The figure depends only on the arguments (and on PA_KV_PARTITION, see below).
+ */
+pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int64_t num_tokens, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                      size_t* bytes);
+
+/*
+ * Attention over one mixed step. The caches must already hold this step's tokens
+ * (call pa_reshape_and_cache first on the same stream). For each row t of sequence i
+ * (position p = context_lens[i] + t - qsl[i]) and query head h (kv head g = h / G):
+ *   s_j        = scale * dot(q[t][h], K_i[j][g])            for j = 0..p
+ *   out[t][h]  = sum_j exp(s_j - max s) V_i[j][g] / sum_j exp(s_j - max s)
+ * where K_i[j] / V_i[j] are the key / value of logical token j of sequence i.
+ * The result is rounded once to the payload dtype (round to nearest even).
+ * Rows t >= qsl[S] of out are not written. Sequences with no rows are skipped.
+ * workspace: device memory of at least pa_attention_workspace_size() bytes, 256-byte
+ * aligned; its contents on entry do not matter. Calls that share a workspace must
+ * not overlap in time.
+ * Environment: PA_KV_PARTITION=<tokens> (a multiple of 32 in [32, 65536]) overrides
+ * the split-KV partition length that decode rows use.
+ * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED, PA_E_ALIGN,
+ * PA_E_WORKSPACE, PA_E_HIP.
+ */
+pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, const int32_t* context_lens, float scale,
+                       void* out, int32_t num_seqs, int32_t max_blocks_per_seq,
+                       int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int64_t num_blocks, pa_dtype dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement support. While enabled, every kernel the library launches is bracketed
+ * by HIP events on its stream. pa_timing_read waits for the recorded events and returns
+ * the summed duration (ms) and the launch count of one kernel kind since the last reset.
+ * Kernel kinds: see pa_kernel_kind. Not for concurrent use from several host threads.
+ */
+typedef enum pa_kernel_kind {
+  PA_KERNEL_SLOT_MAPPING = 0,
+  PA_KERNEL_SCATTER = 1,
+  PA_KERNEL_PLAN = 2,
+  PA_KERNEL_DECODE = 3,
+  PA_KERNEL_REDUCE = 4,
+  PA_KERNEL_PREFILL = 5,
+  PA_KERNEL_ATTN_F32 = 6,
+  PA_KERNEL_KIND_COUNT = 7
+} pa_kernel_kind;
+
+pa_status pa_timing_enable(int enable);
+pa_status pa_timing_reset(void);
+pa_status pa_timing_read(int kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

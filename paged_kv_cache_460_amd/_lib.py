@@ -1,0 +1,80 @@
+"""ctypes view of libpa.so (declarations mirror include/pa.h)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+PA_F32, PA_BF16 = 0, 1
+BLOCK_SIZE = 16
+
+STATUS_NAMES = {
+    0: "PA_OK",
+    1: "PA_E_NULL",
+    2: "PA_E_DTYPE",
+    3: "PA_E_SHAPE",
+    4: "PA_E_UNSUPPORTED",
+    5: "PA_E_ALIGN",
+    6: "PA_E_WORKSPACE",
+    7: "PA_E_HIP",
+}
+
+KERNEL_KINDS = {
+    "slot_mapping": 0,
+    "scatter": 1,
+    "plan": 2,
+    "decode": 3,
+    "reduce": 4,
+    "prefill": 5,
+    "attn_f32": 6,
+}
+
+# name -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_int, []),
+    "pa_build_slot_mapping": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I64, _P, _P, _P]),
+    "pa_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, ctypes.c_int, _P]),
+    "pa_attention_workspace_size": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "pa_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I64, _I32,
+                                    _I32, _I32, _I64, ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "pa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "pa_timing_reset": (ctypes.c_int, []),
+    "pa_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
+}
+
+_lib = None
+
+
+class LibraryMissing(ImportError):
+    """libpa.so has not been built (run ``python -m paged_kv_cache_460_amd.build``)."""
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa.so once; raises LibraryMissing if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} not found: build it with `python -m paged_kv_cache_460_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_names():
+    return list(_SIGNATURES)

@@ -1,0 +1,216 @@
+// Split-KV decode attention on bf16 MFMA (gfx950).
+//
+// Decode is bound by memory bandwidth, prefill by compute (restatement of "Inside vLLM",
+// section 一, scheduler; shengyayun.com blog, 适用场景 and 关键实现细节 item 4). A decode
+// row reads every cached K/V byte of its sequence once, so this kernel is built to
+// stream whole 16-token blocks from HBM at full rate:
+//
+//  * one wave = one (sequence, kv partition of P tokens, kv head). All G query heads of
+//    the kv head ride in the N dimension of one 16x16x32 MFMA, so each K/V byte is
+//    read once for the whole GQA group (columns past G are zero and ignored);
+//  * transposed products: S^T = K Q^T (A = 16 keys x 32 dims straight from the block's
+//    token-major key rows, 16 contiguous bytes per lane) and O^T = V^T P^T, where the
+//    QK accumulator already holds P^T in the B-operand layout, and the dim-major value
+//    block gives each lane 2 x 8 contiguous bytes of V^T (4 keys of block 0, 4 of block 1);
+//  * two blocks (32 keys) per step, with the next step's loads in flight while the
+//    current one computes;
+//  * online softmax in the log2 domain (scale * log2 e folded once), max/sum over the
+//    four lane groups by cross-lane shuffles;
+//  * masked keys are removed by select (-inf score, zeroed value), never by multiplying,
+//    so unwritten slots that hold NaN cannot leak;
+//  * a sequence with a single partition writes its output row directly; otherwise the
+//    wave writes (o, m, l) partials and pa::reduce merges them.
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct DecodeStep {
+  bf16x8 k0[D / 32], k1[D / 32];   // A operands: keys of block 0 / block 1
+  u32x2 v0[D / 16], v1[D / 16];    // halves of the V^T A operands
+};
+
+__device__ inline bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+template <int D>
+__device__ inline void load_step(DecodeStep<D>& s, const uint16_t* __restrict__ kc,
+                                 const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
+                                 int kb, int kend, int hkv, int g, int c, int qd) {
+  const int b0 = kb >> 4;
+  const bool has1 = kb + kBlock < kend;
+  const int64_t p0 = bt[b0];
+  const uint16_t* kr0 = kc + ((p0 * hkv + g) * kBlock + c) * D + qd * 8;
+  const uint16_t* vr0 = vc + ((p0 * hkv + g) * D + c) * kBlock + qd * 4;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) s.k0[kk] = *reinterpret_cast<const bf16x8*>(kr0 + kk * 32);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) s.v0[dt] = *reinterpret_cast<const u32x2*>(vr0 + dt * 16 * kBlock);
+  if (has1) {
+    const int64_t p1 = bt[b0 + 1];
+    const uint16_t* kr1 = kc + ((p1 * hkv + g) * kBlock + c) * D + qd * 8;
+    const uint16_t* vr1 = vc + ((p1 * hkv + g) * D + c) * kBlock + qd * 4;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) s.k1[kk] = *reinterpret_cast<const bf16x8*>(kr1 + kk * 32);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) s.v1[dt] = *reinterpret_cast<const u32x2*>(vr1 + dt * 16 * kBlock);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) s.k1[kk] = bf16x8{};
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) s.v1[dt] = u32x2{0u, 0u};
+  }
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
+  const int lane = threadIdx.x;
+  const int c = lane & 15;   // MFMA column: query head g*G + c
+  const int qd = lane >> 4;  // lane group: dims qd*8.. of each 32-dim chunk; keys 4qd.. of each block
+  const int hkv = p.num_kv_heads;
+  const int64_t wg = blockIdx.x;
+  const int g = (int)(wg % hkv);
+  const int64_t rest = wg / hkv;
+  const int part = (int)(rest % p.max_parts);
+  const int i = (int)(rest / p.max_parts);
+  const int row = p.qsl[i];
+  if (p.qsl[i + 1] - row != 1) return;
+  const int L = p.seq_lens[i];
+  const int P = p.part_tokens;
+  const int kbeg = part * P;
+  if (kbeg >= L) return;
+  const int kend = min(L, kbeg + P);
+  const int nparts = (L + P - 1) / P;
+  const int G = p.group;
+  const int hq = p.num_q_heads;
+
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(p.k_cache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(p.v_cache);
+  const int32_t* __restrict__ bt = p.block_tables + (int64_t)i * p.max_blocks;
+
+  // B operand Q^T: column c, dims kk*32 + qd*8 .. +8.
+  bf16x8 qb[D / 32];
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((int64_t)row * hq + g * G + min(c, G - 1)) * D + qd * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + kk * 32);
+      qb[kk] = (c < G) ? x : bf16x8{};
+    }
+  }
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;
+  float lsum = 0.f;
+  const float sl2 = p.scale * kLog2e;
+
+  DecodeStep<D> cur;
+  load_step<D>(cur, kc, vc, bt, kbeg, kend, hkv, g, c, qd);
+  for (int kb = kbeg; kb < kend; kb += 2 * kBlock) {
+    DecodeStep<D> nxt;
+    const bool more = kb + 2 * kBlock < kend;
+    if (more) load_step<D>(nxt, kc, vc, bt, kb + 2 * kBlock, kend, hkv, g, c, qd);
+
+    // S^T for the two blocks: lane holds keys 4qd..4qd+3 of each block, column c.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k0[kk], qb[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k1[kk], qb[kk], s1, 0, 0, 0);
+    }
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = s0[e] * sl2;
+      sv[4 + e] = s1[e] * sl2;
+    }
+    const bool tail = kb + 2 * kBlock > kend;
+    uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kb + (e >> 2) * kBlock + 4 * qd + (e & 3);
+        if (key >= kend) {
+          sv[e] = -INFINITY;
+          vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    float pe[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
+      psum += pe[e];
+    }
+    lsum = lsum * alpha + psum;
+    m = mnew;
+    const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
+                      pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
+    const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      u32x4 vw = {cur.v0[dt][0], cur.v0[dt][1], cur.v1[dt][0], cur.v1[dt][1]};
+      if (tail) {
+        vw[0] &= vmask[0];
+        vw[1] &= vmask[1];
+        vw[2] &= vmask[2];
+        vw[3] &= vmask[3];
+      }
+      acc[dt] *= alpha;
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pb, acc[dt], 0, 0, 0);
+    }
+    if (more) cur = nxt;
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  if (c >= G) return;
+  const int h = g * G + c;
+  if (nparts == 1) {
+    const float inv = 1.0f / lsum;
+    uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)row * hq + h) * D + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                       pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + dt * 16) = w;
+    }
+  } else {
+    const int64_t slot = ((int64_t)i * p.max_parts + part) * hq + h;
+    float* po = p.part_o + slot * D + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt];
+    if (qd == 0) {
+      p.part_ml[slot * 2 + 0] = m;
+      p.part_ml[slot * 2 + 1] = lsum;
+    }
+  }
+}
+
+hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.num_seqs * p.max_parts * p.num_kv_heads;
+  if (grid == 0) return hipSuccess;
+  if (p.head_dim == 128) {
+    hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,337 @@
+// C entry points of libpa: argument validation, workspace carve-up, kernel sequencing,
+// error reporting and optional per-kernel event timing. Declared in include/pa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status fail(pa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int elem_bytes(pa_dtype dt) { return dt == PA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dt) { return dt == PA_F32 || dt == PA_BF16; }
+
+// ---- per-kernel event timing ----------------------------------------------------
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  struct Pending {
+    int kind;
+    hipEvent_t start, stop;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double total_ms[PA_KERNEL_KIND_COUNT] = {};
+  int64_t launches[PA_KERNEL_KIND_COUNT] = {};
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+// Launch `fn` (returns hipError_t), bracketed by events when timing is on.
+template <class F>
+hipError_t timed(int kind, hipStream_t stream, F&& fn) {
+  Timing& t = timing();
+  if (!t.enabled) return fn();
+  std::lock_guard<std::mutex> lock(t.mu);
+  hipEvent_t a = t.take(), b = t.take();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, stream);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, stream);
+  if (e != hipSuccess) return e;
+  t.pending.push_back({kind, a, b});
+  return hipSuccess;
+}
+
+}  // namespace
+
+namespace pa {
+
+int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads) {
+  if (const char* env = std::getenv("PA_KV_PARTITION")) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v >= 32 && v <= 65536 && v % 32 == 0) return (int32_t)v;
+  }
+  // Largest partition that still leaves >= 16K (sequence, partition, kv head) tasks
+  // when every sequence is as long as its block table allows; never below 256 tokens.
+  const int64_t max_len = (int64_t)max_blocks * kBlock;
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  for (int32_t P = 1024; P >= 256; P /= 2) {
+    const int64_t tasks = pairs * ((max_len + P - 1) / P);
+    if (tasks >= 16384) return P;
+  }
+  return 256;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_q_heads,
+                                 int32_t head_dim, pa_dtype dtype, int32_t part_tokens) {
+  WorkspaceLayout w{};
+  if (dtype != PA_BF16 || num_seqs == 0) return w;  // the fp32 path needs no workspace
+  size_t off = 0;
+  w.tile_offsets = off;
+  off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
+  const int64_t max_parts = ((int64_t)max_blocks * kBlock + part_tokens - 1) / part_tokens;
+  if (max_parts > 1) {
+    const size_t slots = (size_t)num_seqs * (size_t)max_parts * (size_t)num_q_heads;
+    w.part_o = off;
+    off += align256(slots * (size_t)head_dim * sizeof(float));
+    w.part_ml = off;
+    off += align256(slots * 2 * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_E_NULL: return "PA_E_NULL: required pointer is NULL";
+    case PA_E_DTYPE: return "PA_E_DTYPE: unknown dtype";
+    case PA_E_SHAPE: return "PA_E_SHAPE: invalid or inconsistent size";
+    case PA_E_UNSUPPORTED: return "PA_E_UNSUPPORTED: shape not provided by this build";
+    case PA_E_ALIGN: return "PA_E_ALIGN: payload pointer not 16-byte aligned";
+    case PA_E_WORKSPACE: return "PA_E_WORKSPACE: workspace missing or too small";
+    case PA_E_HIP: return "PA_E_HIP: HIP runtime error";
+  }
+  return "unknown pa_status";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_version(void) { return PA_VERSION; }
+
+pa_status pa_build_slot_mapping(const int32_t* block_tables, const int32_t* query_start_loc,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_blocks_per_seq, int64_t num_tokens, int32_t* positions,
+                                int64_t* slot_mapping, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0) return fail(PA_E_SHAPE, "num_seqs=%d num_tokens=%lld must be >= 0", num_seqs, (long long)num_tokens);
+  if (num_seqs > 0 && max_blocks_per_seq < 1) return fail(PA_E_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
+  if (num_tokens > ((int64_t)1 << 31) * 255) return fail(PA_E_SHAPE, "num_tokens=%lld too large", (long long)num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !query_start_loc) return fail(PA_E_NULL, "slot_mapping and query_start_loc are required");
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PA_E_NULL, "block_tables and context_lens are required");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(PA_KERNEL_SLOT_MAPPING, s, [&] {
+    return pa::launch_slot_mapping(block_tables, query_start_loc, context_lens, num_seqs, max_blocks_per_seq,
+                                   num_tokens, positions, slot_mapping, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "slot mapping launch");
+  return PA_OK;
+}
+
+pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int64_t num_blocks, pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return fail(PA_E_DTYPE, "dtype=%d is not PA_F32 or PA_BF16", (int)dtype);
+  if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || num_blocks < 1)
+    return fail(PA_E_SHAPE, "num_tokens=%lld num_kv_heads=%d head_dim=%d num_blocks=%lld out of range",
+                (long long)num_tokens, num_kv_heads, head_dim, (long long)num_blocks);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_E_UNSUPPORTED, "head_dim=%d (64 or 128 supported)", head_dim);
+  const int eb = elem_bytes(dtype);
+  const int64_t threads = num_tokens * num_kv_heads * (int64_t)(head_dim * eb / 16);
+  if (threads > ((int64_t)1 << 31) * 255) return fail(PA_E_SHAPE, "step too large for one launch");
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_E_NULL, "k, v, k_cache, v_cache and slot_mapping are required");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_E_ALIGN, "k, v, k_cache and v_cache must be 16-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(PA_KERNEL_SCATTER, s, [&] {
+    return pa::launch_scatter(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, eb, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "scatter launch");
+  return PA_OK;
+}
+
+static pa_status check_attention_sizes(int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_tokens,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int dtype) {
+  if (!valid_dtype(dtype)) return fail(PA_E_DTYPE, "dtype=%d is not PA_F32 or PA_BF16", dtype);
+  if (num_seqs < 0 || num_tokens < 0) return fail(PA_E_SHAPE, "num_seqs=%d num_tokens=%lld must be >= 0", num_seqs, (long long)num_tokens);
+  if (num_seqs > 0 && max_blocks_per_seq < 1) return fail(PA_E_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
+  if (max_blocks_per_seq > (1 << 26)) return fail(PA_E_SHAPE, "max_blocks_per_seq=%d too large", max_blocks_per_seq);
+  if (num_q_heads < 1 || num_kv_heads < 1) return fail(PA_E_SHAPE, "head counts must be >= 1");
+  if (num_q_heads % num_kv_heads) return fail(PA_E_SHAPE, "num_q_heads=%d is not a multiple of num_kv_heads=%d", num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16) return fail(PA_E_UNSUPPORTED, "group size %d (1..16 supported)", num_q_heads / num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_E_UNSUPPORTED, "head_dim=%d (64 or 128 supported)", head_dim);
+  if (num_tokens > (int64_t)INT32_MAX / 2) return fail(PA_E_SHAPE, "num_tokens=%lld too large", (long long)num_tokens);
+  return PA_OK;
+}
+
+pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_tokens,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      pa_dtype dtype, size_t* bytes) {
+  if (!bytes) return fail(PA_E_NULL, "bytes is required");
+  const pa_status st = check_attention_sizes(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads,
+                                             num_kv_heads, head_dim, dtype);
+  if (st != PA_OK) return st;
+  const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
+  *bytes = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_q_heads, head_dim, dtype, P).total;
+  return PA_OK;
+}
+
+pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                       const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens,
+                       float scale, void* out, int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_tokens,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                       pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = check_attention_sizes(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads,
+                                       head_dim, dtype);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return fail(PA_E_SHAPE, "scale must be finite");
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (num_blocks < 1) return fail(PA_E_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !context_lens || !out)
+    return fail(PA_E_NULL, "q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens and out are required");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_E_ALIGN, "q, out, k_cache and v_cache must be 16-byte aligned");
+
+  pa::AttnParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.qsl = query_start_loc;
+  p.ctx = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.group = num_q_heads / num_kv_heads;
+  p.num_tokens = num_tokens;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (dtype == PA_F32) {
+    const hipError_t e = timed(PA_KERNEL_ATTN_F32, s, [&] { return pa::launch_attn_f32(p, s); });
+    if (e != hipSuccess) return hip_fail(e, "fp32 attention launch");
+    return PA_OK;
+  }
+
+  p.part_tokens = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
+  p.max_parts = (int32_t)(((int64_t)max_blocks_per_seq * pa::kBlock + p.part_tokens - 1) / p.part_tokens);
+  const int64_t decode_grid = (int64_t)num_seqs * p.max_parts * num_kv_heads;
+  if (decode_grid > INT32_MAX) return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)decode_grid);
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_q_heads, head_dim, dtype,
+                                                     p.part_tokens);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", w.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (!aligned16(workspace)) return fail(PA_E_ALIGN, "workspace must be 16-byte aligned");
+  char* base = static_cast<char*>(workspace);
+  p.tile_offsets = reinterpret_cast<int32_t*>(base + w.tile_offsets);
+  p.part_o = p.max_parts > 1 ? reinterpret_cast<float*>(base + w.part_o) : nullptr;
+  p.part_ml = p.max_parts > 1 ? reinterpret_cast<float*>(base + w.part_ml) : nullptr;
+
+  hipError_t e = timed(PA_KERNEL_PLAN, s, [&] { return pa::launch_plan(p, s); });
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  e = timed(PA_KERNEL_DECODE, s, [&] { return pa::launch_decode_bf16(p, s); });
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (p.max_parts > 1) {
+    e = timed(PA_KERNEL_REDUCE, s, [&] { return pa::launch_reduce(p, s); });
+    if (e != hipSuccess) return hip_fail(e, "reduce launch");
+  }
+  e = timed(PA_KERNEL_PREFILL, s, [&] { return pa::launch_prefill_bf16(p, s); });
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return PA_OK;
+}
+
+pa_status pa_timing_enable(int enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.enabled = enable != 0;
+  return PA_OK;
+}
+
+pa_status pa_timing_reset(void) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  for (auto& pd : t.pending) {
+    hipEventSynchronize(pd.stop);
+    t.pool.push_back(pd.start);
+    t.pool.push_back(pd.stop);
+  }
+  t.pending.clear();
+  for (int k = 0; k < PA_KERNEL_KIND_COUNT; ++k) {
+    t.total_ms[k] = 0.0;
+    t.launches[k] = 0;
+  }
+  return PA_OK;
+}
+
+pa_status pa_timing_read(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= PA_KERNEL_KIND_COUNT) return fail(PA_E_SHAPE, "kernel kind %d out of range", kind);
+  if (!total_ms || !launches) return fail(PA_E_NULL, "total_ms and launches are required");
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  for (auto& pd : t.pending) {
+    hipError_t e = hipEventSynchronize(pd.stop);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pd.start, pd.stop);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+    t.total_ms[pd.kind] += ms;
+    t.launches[pd.kind] += 1;
+    t.pool.push_back(pd.start);
+    t.pool.push_back(pd.stop);
+  }
+  t.pending.clear();
+  *total_ms = t.total_ms[kind];
+  *launches = t.launches[kind];
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal declarations shared by the kernels and the C entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kBlock = PA_BLOCK_SIZE;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Rows (query tokens) handled by one prefill workgroup: 4 waves, each owning
+// floor(32 / G) rows x G heads = up to 32 MFMA columns.
+__host__ __device__ inline int prefill_rows_per_wave(int group) { return 32 / group; }
+__host__ __device__ inline int prefill_rows_per_wg(int group) { return 4 * prefill_rows_per_wave(group); }
+
+// Everything the attention kernels read; pointers are device pointers.
+struct AttnParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  const int32_t* ctx;
+  void* out;
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t group;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  float scale;
+  // split-KV decode
+  int32_t part_tokens;   // partition length P (multiple of 32)
+  int32_t max_parts;     // ceil(MB * 16 / P)
+  float* part_o;         // [S, max_parts, Hq, D] unnormalised partial outputs
+  float* part_ml;        // [S, max_parts, Hq, 2]  running max (log2 domain) and sum
+  // prefill work list
+  int32_t* tile_offsets; // [S + 1] exclusive prefix of prefill tiles per sequence
+};
+
+// Workspace carve-up (byte offsets from the workspace base).
+struct WorkspaceLayout {
+  size_t tile_offsets;
+  size_t part_o;
+  size_t part_ml;
+  size_t total;
+};
+
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_q_heads,
+                                 int32_t head_dim, pa_dtype dtype, int32_t part_tokens);
+int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads);
+
+// Kernel launchers (defined next to their kernels). Each returns hipGetLastError().
+hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* qsl, const int32_t* ctx,
+                               int32_t num_seqs, int32_t max_blocks, int64_t num_tokens,
+                               int32_t* positions, int64_t* slots, hipStream_t stream);
+hipError_t launch_scatter(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int64_t* slots, int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_plan(const AttnParams& p, hipStream_t stream);
+hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_reduce(const AttnParams& p, hipStream_t stream);
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+
+// --- small device helpers ---------------------------------------------------
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bfloat16 bits (NaN stays NaN).
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Largest i in [0, n) with a[i] <= x, for non-decreasing a[0..n] and a[0] <= x < a[n].
+__device__ inline int upper_index(const int32_t* a, int n, int64_t x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace pa

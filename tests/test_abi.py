@@ -1,0 +1,168 @@
+"""libpa's C boundary without a GPU: exports, status strings, host-side validation.
+
+Every call here fails validation (or has nothing to do) before anything reaches the
+HIP runtime, so no device is needed. Pointer arguments are fake but are never
+dereferenced: validation rejects the call first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_460_amd as pa
+from paged_kv_cache_460_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+
+P = ctypes.c_void_p
+A = P(0x10000)  # aligned, never dereferenced
+A2 = P(0x20000)
+MIS = P(0x10008)  # 8-byte aligned only
+
+OK, E_NULL, E_DTYPE, E_SHAPE, E_UNSUP, E_ALIGN, E_WS, E_HIP = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libpa.so not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_functions():
+    assert header_functions() == sorted(_lib.exported_names())
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    nm = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}$", nm, re.M), f"{name} is not a defined text symbol"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pa_version() == 1
+    for code in range(8):
+        s = lib.pa_status_string(code).decode()
+        assert s.startswith(_lib.STATUS_NAMES[code])
+    assert lib.pa_status_string(99).decode().startswith("unknown")
+
+
+def attention(lib, q=A, kc=A, vc=A, bt=A, sl=A, qsl=A, ctx=A, scale=0.125, out=A2, S=4, MB=4, T=4, hq=4,
+              hkv=1, d=64, nb=32, dtype=1, ws=None, ws_bytes=0):
+    return lib.pa_attention(q, kc, vc, bt, sl, qsl, ctx, ctypes.c_float(scale), out, S, MB, T, hq, hkv, d, nb,
+                            dtype, ws if ws is not None else P(0), ws_bytes, P(0))
+
+
+def test_attention_validation(lib):
+    assert attention(lib, dtype=7) == E_DTYPE
+    assert attention(lib, d=96) == E_UNSUP
+    assert attention(lib, hq=6, hkv=4) == E_SHAPE
+    assert attention(lib, hq=64, hkv=2) == E_UNSUP          # group of 32
+    assert attention(lib, S=-1) == E_SHAPE
+    assert attention(lib, T=-3) == E_SHAPE
+    assert attention(lib, MB=0) == E_SHAPE
+    assert attention(lib, nb=0) == E_SHAPE
+    assert attention(lib, scale=float("nan")) == E_SHAPE
+    assert attention(lib, q=P(0)) == E_NULL
+    assert attention(lib, bt=P(0)) == E_NULL
+    assert attention(lib, out=P(0)) == E_NULL
+    assert attention(lib, q=MIS) == E_ALIGN
+    assert attention(lib, out=MIS) == E_ALIGN
+    assert "16-byte" in lib.pa_last_error().decode()
+    # bf16 needs a workspace; too small or missing is rejected before any launch
+    assert attention(lib, ws=None) == E_WS
+    assert attention(lib, ws=A, ws_bytes=8) == E_WS
+    assert "workspace" in lib.pa_last_error().decode()
+    # nothing to do: OK without touching the device
+    assert attention(lib, S=0, T=0) == OK
+    assert attention(lib, T=0) == OK
+
+
+def test_workspace_size(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.pa_attention_workspace_size(64, 256, 64, 32, 8, 128, 1, ctypes.byref(out)) == OK
+    bf16 = out.value
+    assert bf16 > 0 and bf16 % 256 == 0
+    assert lib.pa_attention_workspace_size(64, 256, 64, 32, 8, 128, 0, ctypes.byref(out)) == OK
+    assert out.value == 0  # the fp32 path takes no workspace
+    assert lib.pa_attention_workspace_size(64, 256, 64, 32, 8, 96, 1, ctypes.byref(out)) == E_UNSUP
+    assert lib.pa_attention_workspace_size(64, 256, 64, 32, 8, 128, 1, None) == E_NULL
+    # larger block tables need at least as much
+    assert lib.pa_attention_workspace_size(64, 512, 64, 32, 8, 128, 1, ctypes.byref(out)) == OK
+    assert out.value >= bf16
+
+
+def test_reshape_and_cache_validation(lib):
+    def call(k=A, v=A, kc=A, vc=A, sm=A, T=4, hkv=2, d=128, nb=8, dt=1):
+        return lib.pa_reshape_and_cache(k, v, kc, vc, sm, T, hkv, d, nb, dt, P(0))
+
+    assert call(dt=3) == E_DTYPE
+    assert call(d=80) == E_UNSUP
+    assert call(T=-1) == E_SHAPE
+    assert call(hkv=0) == E_SHAPE
+    assert call(nb=0) == E_SHAPE
+    assert call(sm=P(0)) == E_NULL
+    assert call(kc=MIS) == E_ALIGN
+    assert call(T=0) == OK
+
+
+def test_slot_mapping_validation(lib):
+    def call(bt=A, qsl=A, ctx=A, S=2, MB=3, T=5, pos=A, sm=A):
+        return lib.pa_build_slot_mapping(bt, qsl, ctx, S, MB, T, pos, sm, P(0))
+
+    assert call(S=-1) == E_SHAPE
+    assert call(MB=0) == E_SHAPE
+    assert call(sm=P(0)) == E_NULL
+    assert call(bt=P(0)) == E_NULL
+    assert call(T=0) == OK
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+
+    attention(lib, d=96)
+    main_msg = lib.pa_last_error().decode()
+    seen = {}
+
+    def worker():
+        seen["before"] = lib.pa_last_error().decode()
+        attention(lib, dtype=9)
+        seen["after"] = lib.pa_last_error().decode()
+
+    th = threading.Thread(target=worker)
+    th.start()
+    th.join()
+    assert seen["before"] == ""
+    assert "dtype" in seen["after"]
+    assert lib.pa_last_error().decode() == main_msg
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    q = torch.zeros(4, 4, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.attention(q, torch.zeros(2, 1, 16, 64), torch.zeros(2, 1, 64, 16), torch.zeros(4, 1, dtype=torch.int32),
+                     torch.ones(4, dtype=torch.int32), torch.arange(5, dtype=torch.int32),
+                     torch.zeros(4, dtype=torch.int32), 0.125)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.reshape_and_cache(torch.zeros(1, 1, 64), torch.zeros(1, 1, 64), torch.zeros(2, 1, 16, 64),
+                             torch.zeros(2, 1, 64, 16), torch.zeros(1, dtype=torch.int64))
+
+
+def test_product_path_does_not_reference_the_oracle():
+    pkg = os.path.dirname(pa.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(root, f), errors="replace").read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"
