@@ -300,7 +300,7 @@ pa_status pa_timing_reset(void) {
   Timing& t = timing();
   std::lock_guard<std::mutex> lock(t.mu);
   for (auto& pd : t.pending) {
-    hipEventSynchronize(pd.stop);
+    (void)hipEventSynchronize(pd.stop);
     t.pool.push_back(pd.start);
     t.pool.push_back(pd.stop);
   }

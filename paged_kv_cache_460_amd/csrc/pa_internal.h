@@ -15,11 +15,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Rows (query tokens) handled by one prefill workgroup: 4 waves, each owning
-// floor(32 / G) rows x G heads = up to 32 MFMA columns.
-__host__ __device__ inline int prefill_rows_per_wave(int group) { return 32 / group; }
-__host__ __device__ inline int prefill_rows_per_wg(int group) { return 4 * prefill_rows_per_wave(group); }
+// Query rows handled by one prefill workgroup for group size G (defined beside the
+// prefill kernel; the planner cuts chunks into tiles of this many rows).
+int prefill_rows_per_tile(int group);
 
 // Everything the attention kernels read; pointers are device pointers.
 struct AttnParams {
@@ -84,8 +85,10 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats -> two round-to-nearest-even bfloat16 in one word (lo in bits 0..15);
+// a single v_cvt_pk_bf16_f32 on gfx950.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Largest i in [0, n) with a[i] <= x, for non-decreasing a[0..n] and a[0] <= x < a[n].

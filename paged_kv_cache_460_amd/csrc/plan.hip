@@ -3,7 +3,7 @@
 // A step mixes decode rows (one new token) with chunks of long prompts (restatement
 // section 一, scheduler; section 二, item 1). Decode sequences need no list: the decode
 // grid covers (sequence, partition, kv head) and idle entries exit at once. Chunk
-// sequences (two or more rows) are cut into tiles of prefill_rows_per_wg(G) rows; this
+// sequences (two or more rows) are cut into tiles of prefill_rows_per_tile(G) rows; this
 // kernel writes the exclusive prefix sum of tiles per sequence, so the prefill kernel
 // can map a flat task index to (sequence, tile) with no host round trip.
 //
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 
 hipError_t launch_plan(const AttnParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p.qsl, p.num_seqs,
-                     prefill_rows_per_wg(p.group), p.tile_offsets);
+                     prefill_rows_per_tile(p.group), p.tile_offsets);
   return hipGetLastError();
 }
 

@@ -2,24 +2,37 @@
 //
 // Long prompts run in chunks, so a chunk's rows attend to the prompt's cached context
 // plus the chunk's own earlier rows (restatement of "Inside vLLM", section 二, item 1;
-// shengyayun.com blog, MVP step with the long-prefill threshold). Prefill is the
-// compute-bound side of the step (restatement section 一, scheduler), and the only
-// dense contraction of the path, so it runs on the matrix cores.
+// shengyayun.com blog, MVP steps, long-prefill threshold). Prefill is the compute-bound
+// side of the step (restatement section 一, scheduler) and the only dense contraction
+// of the path, so it runs on the matrix cores.
 //
-// Work unit: (chunk sequence, tile of R rows, kv head). The R rows x G query heads of
-// one kv head share every K/V tile, which is staged once in LDS per workgroup:
-//  * 4 waves; wave w owns rows [w*RW, (w+1)*RW) of the tile (RW = 32/G) x all G heads,
-//    i.e. up to 32 MFMA columns;
-//  * keys move in tiles of 64 (4 blocks), gathered through the block table;
-//  * S^T = K Q^T and O^T = V^T P^T on 32x32x16 MFMA, so the QK accumulator is already
-//    the B operand of PV (see the decode kernel for the same pairing);
-//  * online softmax in the log2 domain; causal and end-of-sequence keys are removed by
-//    select, and value rows of keys past the sequence end are zeroed when staged, so
-//    NaN in unwritten slots cannot leak;
-//  * tasks are taken in reverse flat order: last sequence first, last rows first
-//    (for the usual ascending-context chunk order, the longest tiles start first);
-//  * the kv head is the fastest-varying task index, so with 8 kv heads and a grid that
-//    is a multiple of 8, all tiles of one kv head run on one XCD and share its L2.
+// Work unit: one workgroup = (chunk sequence, tile of R rows, kv head). The query
+// "columns" of a kv head are (row, head-in-group) pairs; a strip is 32 of them
+// (32 / G rows x G heads, one MFMA N-tile). Each of the NW waves owns NS strips, so
+// R = NW * NS * (32 / G) rows. The K/V tiles of the kv head are staged once in LDS and
+// shared by every strip of the workgroup.
+//
+// Per key tile of 64 keys (4 blocks, gathered through the block table):
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read from LDS,
+//    B = Q^T held in registers for the whole tile loop;
+//  * the key rows are fed to the MFMA in a fixed permuted order, chosen so that the
+//    accumulator elements a lane holds are 8 consecutive keys of one block: they are
+//    then directly the B operand of O^T = V^T P^T, and the matching A operand is one
+//    16-byte read of the dim-major value tile (8 consecutive tokens of one dimension);
+//  * online softmax in the log2 domain with a lazily raised running max: the output is
+//    rescaled only when some column's max grows by more than 2^8, which after the first
+//    tiles is rare. Exact either way: the same max is used for the weights and the sum;
+//  * masked keys (causal, or past the sequence end) are removed by select, and value
+//    entries past the sequence end are zeroed while staging, so NaN in unwritten slots
+//    cannot leak.
+// Tiles are staged through registers with one tile of prefetch: the loads of tile t+1
+// are in flight while tile t is multiplied, and one barrier per tile separates the two
+// LDS buffers. (Two waves share each SIMD, so one wave's softmax overlaps the other's
+// MFMAs when they drift apart.) LDS tiles are XOR-swizzled in 16-byte units so that the 16-byte operand
+// reads of a half-wave hit distinct banks.
+//
+// Workgroups take tasks last-first: last sequence, last rows first, kv head fastest.
+// For chunks listed in ascending-context order that starts the longest tiles first.
 #include <algorithm>
 
 #include "pa_internal.h"
@@ -27,224 +40,341 @@
 namespace pa {
 
 namespace {
+
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRescale = 8.0f;  // log2 of the largest weight let through unscaled
+constexpr int kTK = 64;              // keys per tile
+
 __device__ inline bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// Key row (within a 32-key half tile) that MFMA row m reads; see the header comment.
+__device__ inline int perm_key(int m) {
+  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+// 16-byte-unit swizzles of the LDS tiles.
+template <int D>
+__device__ inline int key_swz(int row) {
+  return (row / (128 / D)) & (D / 8 - 1);
+}
+__device__ inline int val_swz(int dim) { return (dim >> 3) & 1; }
+
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(AttnParams p) {
-  constexpr int TK = 64;       // keys per tile (4 blocks)
-  constexpr int KS = D + 8;    // LDS row stride of a key row (elements): staggers banks
-  constexpr int VS = 20;       // LDS row stride of a value row (16 keys + 4 pad)
-  constexpr int KCH = 4 * kBlock * (D / 8);  // 16-byte chunks per key tile
-  constexpr int VCH = 4 * D * 2;              // 16-byte chunks per value tile
-  static_assert(KCH % 256 == 0 && VCH % 256 == 0, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) uint16_t ks[TK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[4 * D * VS];
+template <int D, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnParams p) {
+  constexpr int CPR = D / 8;                      // 16-byte chunks per key row
+  constexpr int KCH = kTK * CPR;                  // chunks per key tile
+  constexpr int VCH = (kTK / kBlock) * D * 2;     // chunks per value tile
+  constexpr int NT = NW * 64;
+  static_assert(KCH % NT == 0 && VCH % NT == 0, "tile must split evenly over the workgroup");
+  constexpr int KPT = KCH / NT;
+  constexpr int VPT = VCH / NT;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kTK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kTK * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int col = lane & 31;   // MFMA column (query row x head)
-  const int h2 = lane >> 5;    // lane half
+  const int col = lane & 31;  // MFMA column within a strip
+  const int h2 = lane >> 5;   // lane half
   const int G = p.group;
   const int hkv = p.num_kv_heads;
   const int hq = p.num_q_heads;
   const int RW = 32 / G;
-  const int R = 4 * RW;
+  const int R = NW * NS * RW;
   const int S = p.num_seqs;
   const int total_tiles = p.tile_offsets[S];
-  const int64_t ntasks = (int64_t)total_tiles * hkv;
+  const int64_t u = blockIdx.x;
+  if (u >= (int64_t)total_tiles * hkv) return;
+
+  const int g = (int)(u % hkv);
+  const int tile = total_tiles - 1 - (int)(u / hkv);
+  const int i = upper_index(p.tile_offsets, S, tile);
+  const int rt = tile - p.tile_offsets[i];
+  const int q0 = p.qsl[i];
+  const int n = p.qsl[i + 1] - q0;
+  const int ctx = p.ctx[i];
+  const int L = p.seq_lens[i];
+  const int r0 = rt * R;
+  const int kmax = ctx + min(r0 + R, n);  // keys [0, kmax) are seen by some row of the tile
+  const int32_t* __restrict__ bt = p.block_tables + (int64_t)i * p.max_blocks;
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(p.k_cache);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(p.v_cache);
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
   uint16_t* __restrict__ og = static_cast<uint16_t*>(p.out);
-  const float sl2 = p.scale * kLog2e;
+  // A negative scale is folded into the (exactly negated) queries.
+  const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
+  // (floored at a tiny positive value so that masked -inf scores still map to weight 0)
+  const float sl2 = fmaxf(fabsf(p.scale) * kLog2e, 1e-30f);
 
-  for (int64_t u = blockIdx.x; u < ntasks; u += gridDim.x) {
-    const int g = (int)(u % hkv);
-    const int tile = total_tiles - 1 - (int)(u / hkv);
-    const int i = upper_index(p.tile_offsets, S, tile);
-    const int rt = tile - p.tile_offsets[i];
-    const int q0 = p.qsl[i];
-    const int n = p.qsl[i + 1] - q0;
-    const int ctx = p.ctx[i];
-    const int L = p.seq_lens[i];
-    const int r0 = rt * R;
-    const int kmax = ctx + min(r0 + R, n);  // keys [0, kmax) are seen by some row of the tile
-    const int32_t* __restrict__ bt = p.block_tables + (int64_t)i * p.max_blocks;
-
-    const int wr0 = r0 + wave * RW;
-    const int wrows = max(0, min(RW, n - wr0));
-    const int wkmax = wrows > 0 ? ctx + wr0 + wrows : 0;
-    const int crow = wr0 + col / G;
-    const bool cvalid = (col < RW * G) && (crow < n);
-    const int head = g * G + (col % G);
-    const int cpos = cvalid ? ctx + crow : wkmax - 1;
-
-    bf16x8 qb[D / 16];
-    {
-      const uint16_t* qr = qg + ((int64_t)(q0 + (cvalid ? crow : 0)) * hq + head) * D + h2 * 8;
+  // ---- per strip: rows, validity, query operands ----
+  int srow0[NS], skmax[NS], cpos[NS], crow[NS];
+  bool cvalid[NS];
+  bf16x8 qf[NS][D / 16];
+  const int head = g * G + (col % G);
 #pragma unroll
-      for (int kq = 0; kq < D / 16; ++kq) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + kq * 16);
-        qb[kq] = cvalid ? x : bf16x8{};
+  for (int s = 0; s < NS; ++s) {
+    srow0[s] = r0 + (wave * NS + s) * RW;
+    const int srows = max(0, min(RW, n - srow0[s]));
+    skmax[s] = srows > 0 ? ctx + srow0[s] + srows : 0;
+    crow[s] = srow0[s] + col / G;
+    cvalid[s] = (col < RW * G) && (crow[s] < n);
+    // Idle columns mirror the strip's first row so their arithmetic stays finite.
+    cpos[s] = cvalid[s] ? ctx + crow[s] : ctx + srow0[s];
+    const uint16_t* qr = qg + ((int64_t)(q0 + (cvalid[s] ? crow[s] : min(srow0[s], n - 1))) * hq + head) * D + h2 * 8;
+#pragma unroll
+    for (int kq = 0; kq < D / 16; ++kq) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qr + kq * 16);
+      w ^= qsign;
+      qf[s][kq] = cvalid[s] ? as_bf16x8(w) : bf16x8{};
+    }
+  }
+
+  f32x16 o[NS][D / 32];
+  float m[NS], l[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    m[s] = -INFINITY;
+    l[s] = 0.f;
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) o[s][md] = f32x16{};
+  }
+
+  // ---- staging: key tile / value tile of keys [kt, kt + 64) -> registers -> LDS ----
+  u32x4 kreg[KPT], vreg[VPT];
+  auto gather_k = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int ci = tid + NT * j;
+      const int row = ci / CPR;
+      // A block holds 16 * CPR chunks, a multiple of 64, and a wave's 64 chunk indices
+      // are 64-aligned: all lanes of a wave stage the same block, so its id is loaded
+      // once per wave (scalar).
+      const int b = __builtin_amdgcn_readfirstlane((kt + row) >> 4);
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (b * kBlock < L) {
+        const int64_t phys = bt[b];
+        w = *reinterpret_cast<const u32x4*>(kc + ((phys * hkv + g) * kBlock + (row & 15)) * D + (ci % CPR) * 8);
+      }
+      kreg[j] = w;
+    }
+  };
+  auto gather_v = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int ci = tid + NT * j;
+      const int bl = ci / (2 * D);
+      const int dim = (ci >> 1) % D;
+      const int half = ci & 1;
+      // 2 * D chunks per block, a multiple of 64: the block is wave-uniform here too.
+      const int b = __builtin_amdgcn_readfirstlane((kt >> 4) + bl);
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (b * kBlock < L) {
+        const int64_t phys = bt[b];
+        w = *reinterpret_cast<const u32x4*>(vc + ((phys * hkv + g) * D + dim) * kBlock + half * 8);
+        const int key0 = b * kBlock + half * 8;
+        if (key0 + 8 > L) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
+      }
+      vreg[j] = w;
+    }
+  };
+  auto stage_k = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int ci = tid + NT * j;
+      const int row = ci / CPR;
+      const int c = (ci % CPR) ^ key_swz<D>(row);
+      *reinterpret_cast<u32x4*>(&ks[buf][row * D + c * 8]) = kreg[j];
+    }
+  };
+  auto stage_v = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int ci = tid + NT * j;
+      const int bl = ci / (2 * D);
+      const int dim = (ci >> 1) % D;
+      const int half = (ci & 1) ^ val_swz(dim);
+      *reinterpret_cast<u32x4*>(&vs[buf][(bl * D + dim) * kBlock + half * 8]) = vreg[j];
+    }
+  };
+
+  // ---- S^T = K Q^T for the 64 keys of one staged key tile ----
+  auto qk = [&](int buf, f32x16 (&sc)[NS][2]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sc[s][0] = sc[s][1] = f32x16{};
+    const int row0 = perm_key(col);
+    const uint16_t* kr0 = &ks[buf][row0 * D];
+    const uint16_t* kr1 = &ks[buf][(32 + row0) * D];
+    const int sw0 = key_swz<D>(row0), sw1 = key_swz<D>(32 + row0);
+#pragma unroll
+    for (int kq = 0; kq < D / 16; ++kq) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr0 + (((kq * 2 + h2) ^ sw0) * 8));
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr1 + (((kq * 2 + h2) ^ sw1) * 8));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sc[s][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s][kq], sc[s][0], 0, 0, 0);
+        sc[s][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s][kq], sc[s][1], 0, 0, 0);
       }
     }
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
-    float m = -INFINITY;
-    float l = 0.f;
+  };
 
-    for (int kt = 0; kt < kmax; kt += TK) {
-      // ---- gather the tile: 4 blocks of keys and values ----
-      u32x4 kreg[KCH / 256], vreg[VCH / 256];
+  // ---- online softmax of one tile's scores (log2 domain, lazy rescale) -> P^T ----
+  //   softmax_weights: mask (if asked), running max, weights, packed P^T, partial sums;
+  //   softmax_commit:  the rare rescale of the output, then the running sum.
+  // The weights of a 16-key block feed that block's PV MFMAs, so the compiler overlaps
+  // the exponentials of later blocks with the MFMAs of earlier ones.
+  auto softmax_weights = [&](int kt, bool masked, f32x16 (&sc)[NS][2], bf16x8 (&pf)[NS][4], float (&mnew)[NS],
+                             float (&psum)[NS], bool& any_raise) {
+    any_raise = false;
 #pragma unroll
-      for (int j = 0; j < KCH / 256; ++j) {
-        const int chunk = tid + 256 * j;
-        const int bl = chunk / (kBlock * (D / 8));
-        const int key = (chunk / (D / 8)) % kBlock;
-        const int dc = chunk % (D / 8);
-        const int b = (kt >> 4) + bl;
-        if (b * kBlock < L) {
-          const int64_t phys = bt[b];
-          kreg[j] = *reinterpret_cast<const u32x4*>(kc + ((phys * hkv + g) * kBlock + key) * D + dc * 8);
-        } else {
-          kreg[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+    for (int s = 0; s < NS; ++s) {
+      // element r of sc[s][mt] is key kt + mt*32 + 16*(r>>3) + 8*h2 + (r&7)
+      if (masked) {
 #pragma unroll
-      for (int j = 0; j < VCH / 256; ++j) {
-        const int chunk = tid + 256 * j;
-        const int bl = chunk / (2 * D);
-        const int dr = (chunk >> 1) % D;
-        const int half = chunk & 1;
-        const int b = (kt >> 4) + bl;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (b * kBlock < L) {
-          const int64_t phys = bt[b];
-          w = *reinterpret_cast<const u32x4*>(vc + ((phys * hkv + g) * D + dr) * kBlock + half * 8);
-          const int key0 = b * kBlock + half * 8;
-          if (key0 + 8 > L) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-        }
-        vreg[j] = w;
-      }
-      __syncthreads();  // every wave is done reading the previous tile
-#pragma unroll
-      for (int j = 0; j < KCH / 256; ++j) {
-        const int chunk = tid + 256 * j;
-        const int bl = chunk / (kBlock * (D / 8));
-        const int key = (chunk / (D / 8)) % kBlock;
-        const int dc = chunk % (D / 8);
-        *reinterpret_cast<u32x4*>(&ks[(bl * kBlock + key) * KS + dc * 8]) = kreg[j];
-      }
-#pragma unroll
-      for (int j = 0; j < VCH / 256; ++j) {
-        const int chunk = tid + 256 * j;
-        const int bl = chunk / (2 * D);
-        const int dr = (chunk >> 1) % D;
-        const int half = chunk & 1;
-        uint16_t* dst = &vs[(bl * D + dr) * VS + half * 8];
-        *reinterpret_cast<u32x2*>(dst) = u32x2{vreg[j][0], vreg[j][1]};
-        *reinterpret_cast<u32x2*>(dst + 4) = u32x2{vreg[j][2], vreg[j][3]};
-      }
-      __syncthreads();
-
-      if (kt < wkmax) {
-        // ---- S^T = K Q^T for 64 keys x 32 columns ----
-        f32x16 s[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          s[mt] = f32x16{};
-#pragma unroll
-          for (int kq = 0; kq < D / 16; ++kq) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[(mt * 32 + col) * KS + kq * 16 + h2 * 8]);
-            s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kq], s[mt], 0, 0, 0);
-          }
-        }
-        const bool need_mask = kt + TK - 1 > ctx + wr0;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float x = s[mt][r] * sl2;
-            if (need_mask) {
-              const int key = kt + mt * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-              if (key > cpos) x = -INFINITY;
-            }
-            s[mt][r] = x;
-            mx = fmaxf(mx, x);
+            const int key = kt + mt * 32 + 16 * (r >> 3) + 8 * h2 + (r & 7);
+            sc[s][mt][r] = key > cpos[s] ? -INFINITY : sc[s][mt][r];
           }
+      }
+      float mx = sc[s][0][0];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[s][mt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxs = mx * sl2;
+      const bool raise = mxs > m[s] + kLazyRescale;
+      any_raise |= raise;
+      mnew[s] = raise ? mxs : m[s];
+      const float nm = -mnew[s];
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ub = 0; ub < 4; ++ub) {
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][ub >> 1][(ub & 1) * 8 + e], sl2, nm));
+          ps[e & 3] += pe[e];
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        float psum = 0.f;
-        bf16x8 pb[4];
+        const u32x4 w = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
+                         pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
+        pf[s][ub] = as_bf16x8(w);
+      }
+      psum[s] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+  };
+  auto softmax_commit = [&](const float (&mnew)[NS], const float (&psum)[NS], bool any_raise) {
+    if (__builtin_amdgcn_ballot_w64(any_raise)) {
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-          float pe[8];
+      for (int s = 0; s < NS; ++s) {
+        const float alpha = __builtin_amdgcn_exp2f(m[s] - mnew[s]);
+        l[s] *= alpha;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pe[e] = __builtin_amdgcn_exp2f(s[ub >> 1][(ub & 1) * 8 + e] - mnew);
-            psum += pe[e];
-          }
-          const u32x4 w = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
-                           pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
-          pb[ub] = as_bf16x8(w);
-        }
-        l = l * alpha + psum;
-        m = mnew;
-        // ---- O^T += V^T P^T ----
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) {
-          o[mt] *= alpha;
-#pragma unroll
-          for (int ub = 0; ub < 4; ++ub) {
-            const uint16_t* vr = &vs[(ub * D + mt * 32 + col) * VS + 4 * h2];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-            o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), pb[ub], o[mt], 0, 0, 0);
-          }
-        }
+        for (int md = 0; md < D / 32; ++md) o[s][md] *= alpha;
       }
     }
-    l += __shfl_xor(l, 32);
-    if (cvalid) {
-      const float inv = 1.0f / l;
-      uint16_t* orow = og + ((int64_t)(q0 + crow) * hq + head) * D + 4 * h2;
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
+    for (int s = 0; s < NS; ++s) {
+      m[s] = mnew[s];
+      l[s] += psum[s];
+    }
+  };
+
+  // ---- O^T += V^T P^T for one staged value tile ----
+  auto pv = [&](int buf, bf16x8 (&pf)[NS][4]) {
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const u32x2 w = {pack_bf16x2(o[mt][grp * 4 + 0] * inv, o[mt][grp * 4 + 1] * inv),
-                           pack_bf16x2(o[mt][grp * 4 + 2] * inv, o[mt][grp * 4 + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + mt * 32 + grp * 8) = w;
-        }
+    for (int md = 0; md < D / 32; ++md) {
+      const int dim = md * 32 + col;
+      const int sw = val_swz(dim);
+#pragma unroll
+      for (int ub = 0; ub < 4; ++ub) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vs[buf][(ub * D + dim) * kBlock + ((h2 ^ sw) * 8)]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) o[s][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s][ub], o[s][md], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- tile loop ----
+  // The loads of key/value tile t+1 are in flight while tile t is multiplied; the two
+  // LDS buffers alternate and one barrier per tile separates them. Waves whose rows need
+  // no more keys skip the arithmetic but keep staging and meeting the barrier.
+  int wkmax = 0;  // keys this wave's strips need
+  int wtm = 1 << 30;  // first tile that needs the causal mask
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    wkmax = max(wkmax, skmax[s]);
+    // tile t holds keys up to 64t + 63; the strip's first row sits at ctx + srow0
+    wtm = min(wtm, (ctx + srow0[s] + 1) / kTK);
+  }
+
+  gather_k(0);
+  gather_v(0);
+  int buf = 0;
+  for (int kt = 0; kt < kmax; kt += kTK, buf ^= 1) {
+    stage_k(buf);
+    stage_v(buf);
+    __syncthreads();
+    if (kt + kTK < kmax) {
+      gather_k(kt + kTK);
+      gather_v(kt + kTK);
+    }
+    if (kt >= wkmax) continue;
+    f32x16 sc[NS][2];
+    bf16x8 pf[NS][4];
+    float mnew[NS], psum[NS];
+    bool any_raise;
+    qk(buf, sc);
+    softmax_weights(kt, kt / kTK >= wtm, sc, pf, mnew, psum, any_raise);
+    softmax_commit(mnew, psum, any_raise);
+    pv(buf, pf);
+  }
+
+  // ---- epilogue: normalise, round to bf16, write this lane's 4 x 4 dims per 32 ----
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float lt = l[s] + __shfl_xor(l[s], 32);
+    if (!cvalid[s]) continue;
+    const float inv = 1.0f / lt;
+    uint16_t* orow = og + ((int64_t)(q0 + crow[s]) * hq + head) * D + 4 * h2;
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const u32x2 w = {pack_bf16x2(o[s][md][grp * 4 + 0] * inv, o[s][md][grp * 4 + 1] * inv),
+                         pack_bf16x2(o[s][md][grp * 4 + 2] * inv, o[s][md][grp * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + md * 32 + grp * 8) = w;
       }
     }
   }
 }
 
+// Workgroup shape: waves per workgroup and 32-column strips per wave.
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillStrips = 1;
+
+int prefill_rows_per_tile(int group) { return kPrefillWaves * kPrefillStrips * (32 / group); }
+
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.num_tokens < 2) return hipSuccess;
-  const int R = prefill_rows_per_wg(p.group);
+  const int R = prefill_rows_per_tile(p.group);
   // Upper bound on the tiles the planner can emit: every chunk has >= 2 rows.
   const int64_t chunks = std::min<int64_t>(p.num_seqs, p.num_tokens / 2);
   const int64_t tiles = (p.num_tokens + (int64_t)(R - 1) * chunks) / R + 1;
-  int64_t grid = std::min<int64_t>(tiles * p.num_kv_heads, 2048);
-  grid = (grid + 7) / 8 * 8;
+  const int64_t grid = tiles * p.num_kv_heads;
   if (p.head_dim == 128) {
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillWaves, kPrefillStrips>), dim3((unsigned)grid),
+                       dim3(kPrefillWaves * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, kPrefillWaves, kPrefillStrips>), dim3((unsigned)grid),
+                       dim3(kPrefillWaves * 64), 0, stream, p);
   }
   return hipGetLastError();
 }
