@@ -5,9 +5,10 @@
 // row reads every cached K/V byte of its sequence once, so this kernel is built to
 // stream whole 16-token blocks from HBM at full rate:
 //
-//  * one wave = one (sequence, kv partition of P tokens, kv head). All G query heads of
-//    the kv head ride in the N dimension of one 16x16x32 MFMA, so each K/V byte is
-//    read once for the whole GQA group (columns past G are zero and ignored);
+//  * one wave = one (sequence, kv partition of P tokens, kv head), taken in the
+//    planner's longest-first order. All G query heads of the kv head ride in the N
+//    dimension of one 16x16x32 MFMA, so each K/V byte is read once for the whole GQA
+//    group (columns past G are zero and ignored);
 //  * transposed products: S^T = K Q^T (A = 16 keys x 32 dims straight from the block's
 //    token-major key rows, 16 contiguous bytes per lane) and O^T = V^T P^T, where the
 //    QK accumulator already holds P^T in the B-operand layout, and the dim-major value
@@ -36,6 +37,14 @@ struct DecodeStep {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// Value rows are read once per decode row and each load covers whole 128-byte lines
+// (16 dims x 32 bytes): non-temporal (streaming) loads raise the sustained HBM read rate
+// for them. Key loads stay ordinary: one MFMA operand covers only half of each line,
+// and the other half is read by the next load from the cache.
+__device__ inline u32x2 stream_load_u32x2(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
 template <int D>
 __device__ inline void load_step(DecodeStep<D>& s, const uint16_t* __restrict__ kc,
                                  const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
@@ -48,7 +57,7 @@ __device__ inline void load_step(DecodeStep<D>& s, const uint16_t* __restrict__ 
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) s.k0[kk] = *reinterpret_cast<const bf16x8*>(kr0 + kk * 32);
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) s.v0[dt] = *reinterpret_cast<const u32x2*>(vr0 + dt * 16 * kBlock);
+  for (int dt = 0; dt < D / 16; ++dt) s.v0[dt] = stream_load_u32x2(vr0 + dt * 16 * kBlock);
   if (has1) {
     const int64_t p1 = bt[b0 + 1];
     const uint16_t* kr1 = kc + ((p1 * hkv + g) * kBlock + c) * D + qd * 8;
@@ -56,7 +65,7 @@ __device__ inline void load_step(DecodeStep<D>& s, const uint16_t* __restrict__ 
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) s.k1[kk] = *reinterpret_cast<const bf16x8*>(kr1 + kk * 32);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) s.v1[dt] = *reinterpret_cast<const u32x2*>(vr1 + dt * 16 * kBlock);
+    for (int dt = 0; dt < D / 16; ++dt) s.v1[dt] = stream_load_u32x2(vr1 + dt * 16 * kBlock);
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) s.k1[kk] = bf16x8{};
@@ -73,17 +82,19 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
   const int c = lane & 15;   // MFMA column: query head g*G + c
   const int qd = lane >> 4;  // lane group: dims qd*8.. of each 32-dim chunk; keys 4qd.. of each block
   const int hkv = p.num_kv_heads;
+  // Workgroup -> (task from the planner's longest-first list, kv head); kv head fastest,
+  // so the Hkv workgroups of a task read neighbouring 4 KB tiles of the same blocks.
   const int64_t wg = blockIdx.x;
   const int g = (int)(wg % hkv);
-  const int64_t rest = wg / hkv;
-  const int part = (int)(rest % p.max_parts);
-  const int i = (int)(rest / p.max_parts);
+  const int64_t t = wg / hkv;
+  if (t >= *p.dec_count) return;
+  const int task = p.dec_tasks[t];
+  const int part = task % p.max_parts;
+  const int i = task / p.max_parts;
   const int row = p.qsl[i];
-  if (p.qsl[i + 1] - row != 1) return;
   const int L = p.seq_lens[i];
   const int P = p.part_tokens;
   const int kbeg = part * P;
-  if (kbeg >= L) return;
   const int kend = min(L, kbeg + P);
   const int nparts = (L + P - 1) / P;
   const int G = p.group;

@@ -96,15 +96,16 @@ int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_he
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 32 && v <= 65536 && v % 32 == 0) return (int32_t)v;
   }
-  // Largest partition that still leaves >= 16K (sequence, partition, kv head) tasks
-  // when every sequence is as long as its block table allows; never below 256 tokens.
+  // One wave streams one (sequence, partition, kv head); waves share HBM, so a long
+  // partition is a slow task and the last tasks set the tail. Aim for about eight
+  // partitions over the longest sequence the block table allows, keep >= 8192 tasks
+  // when the sequences are that long, and stay within 256..2048 tokens.
   const int64_t max_len = (int64_t)max_blocks * kBlock;
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  for (int32_t P = 1024; P >= 256; P /= 2) {
-    const int64_t tasks = pairs * ((max_len + P - 1) / P);
-    if (tasks >= 16384) return P;
-  }
-  return 256;
+  int32_t P = 2048;
+  while (P > 256 && (int64_t)P * 8 > max_len) P /= 2;
+  while (P > 256 && pairs * ((max_len + P - 1) / P) < 8192) P /= 2;
+  return P;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -117,6 +118,10 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t n
   w.tile_offsets = off;
   off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
   const int64_t max_parts = ((int64_t)max_blocks * kBlock + part_tokens - 1) / part_tokens;
+  w.dec_count = off;
+  off += 256;
+  w.dec_tasks = off;
+  off += align256(sizeof(int32_t) * (size_t)num_seqs * (size_t)max_parts);
   if (max_parts > 1) {
     const size_t slots = (size_t)num_seqs * (size_t)max_parts * (size_t)num_q_heads;
     w.part_o = off;
@@ -264,7 +269,8 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   p.part_tokens = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
   p.max_parts = (int32_t)(((int64_t)max_blocks_per_seq * pa::kBlock + p.part_tokens - 1) / p.part_tokens);
   const int64_t decode_grid = (int64_t)num_seqs * p.max_parts * num_kv_heads;
-  if (decode_grid > INT32_MAX) return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)decode_grid);
+  if (decode_grid > INT32_MAX || (int64_t)num_seqs * p.max_parts > INT32_MAX)
+    return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)decode_grid);
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_q_heads, head_dim, dtype,
                                                      p.part_tokens);
   if (!workspace || workspace_bytes < w.total)
@@ -273,6 +279,8 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   if (!aligned16(workspace)) return fail(PA_E_ALIGN, "workspace must be 16-byte aligned");
   char* base = static_cast<char*>(workspace);
   p.tile_offsets = reinterpret_cast<int32_t*>(base + w.tile_offsets);
+  p.dec_tasks = reinterpret_cast<int32_t*>(base + w.dec_tasks);
+  p.dec_count = reinterpret_cast<int32_t*>(base + w.dec_count);
   p.part_o = p.max_parts > 1 ? reinterpret_cast<float*>(base + w.part_o) : nullptr;
   p.part_ml = p.max_parts > 1 ? reinterpret_cast<float*>(base + w.part_ml) : nullptr;
 

@@ -48,11 +48,15 @@ struct AttnParams {
   float* part_ml;        // [S, max_parts, Hq, 2]  running max (log2 domain) and sum
   // prefill work list
   int32_t* tile_offsets; // [S + 1] exclusive prefix of prefill tiles per sequence
+  int32_t* dec_tasks;    // [S * max_parts] decode tasks, sequence * max_parts + partition
+  int32_t* dec_count;    // [1] number of decode tasks
 };
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WorkspaceLayout {
   size_t tile_offsets;
+  size_t dec_tasks;
+  size_t dec_count;
   size_t part_o;
   size_t part_ml;
   size_t total;

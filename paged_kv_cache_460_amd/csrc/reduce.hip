@@ -4,7 +4,8 @@
 // (log2 domain) and its weight sum l_p. Softmax over the union of the partitions is
 //   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p,
 // an exact rewrite of the single-pass sum; the result is rounded once to bf16.
-// One wave per (sequence, query head); lanes own dims.
+// One wave per (sequence, query head): lanes take partitions for the max and the
+// denominator, then dimensions for the weighted sum (several partitions in flight).
 #include "pa_internal.h"
 
 namespace pa {
@@ -24,20 +25,37 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnParams p) {
   const int nparts = (p.seq_lens[i] + P - 1) / P;
   if (nparts <= 1) return;
   const int64_t base = (int64_t)i * p.max_parts * hq + h;  // slot of partition 0; stride hq
+
+  // Pass 1, lanes over partitions: global max M and the denominator sum_p 2^(m_p - M) l_p.
   float M = -INFINITY;
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, p.part_ml[(base + (int64_t)q * hq) * 2]);
+  for (int q = lane; q < nparts; q += 64) M = fmaxf(M, p.part_ml[(base + (int64_t)q * hq) * 2]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float den = 0.f;
+  for (int q = lane; q < nparts; q += 64) {
+    const int64_t slot = base + (int64_t)q * hq;
+    den += __builtin_amdgcn_exp2f(p.part_ml[slot * 2] - M) * p.part_ml[slot * 2 + 1];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+
+  // Pass 2, lanes over dims: out = sum_p 2^(m_p - M) o_p / den, 8 partitions in flight.
   constexpr int kPer = D / 64;
   float o[kPer];
 #pragma unroll
   for (int x = 0; x < kPer; ++x) o[x] = 0.f;
-  float den = 0.f;
-  for (int q = 0; q < nparts; ++q) {
-    const int64_t slot = base + (int64_t)q * hq;
-    const float w = __builtin_amdgcn_exp2f(p.part_ml[slot * 2] - M);
-    den += w * p.part_ml[slot * 2 + 1];
-    const float* po = p.part_o + slot * D + lane * kPer;
+  for (int q0 = 0; q0 < nparts; q0 += 8) {
 #pragma unroll
-    for (int x = 0; x < kPer; ++x) o[x] += w * po[x];
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + u;
+      if (q < nparts) {
+        const int64_t slot = base + (int64_t)q * hq;
+        const float w = __builtin_amdgcn_exp2f(p.part_ml[slot * 2] - M);
+        const float* po = p.part_o + slot * D + lane * kPer;
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) o[x] += w * po[x];
+      }
+    }
   }
   const float inv = 1.0f / den;
   uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)row * hq + h) * D + lane * kPer;
