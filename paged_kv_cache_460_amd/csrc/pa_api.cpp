@@ -183,8 +183,8 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
                 (long long)num_tokens, num_kv_heads, head_dim, (long long)num_blocks);
   if (head_dim != 64 && head_dim != 128) return fail(PA_E_UNSUPPORTED, "head_dim=%d (64 or 128 supported)", head_dim);
   const int eb = elem_bytes(dtype);
-  const int64_t threads = num_tokens * num_kv_heads * (int64_t)(head_dim * eb / 16);
-  if (threads > ((int64_t)1 << 31) * 255) return fail(PA_E_SHAPE, "step too large for one launch");
+  const int64_t groups = (num_tokens + 15) / 16 * (int64_t)num_kv_heads;  // scatter workgroups
+  if (groups > INT32_MAX) return fail(PA_E_SHAPE, "step too large for one launch");
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_E_NULL, "k, v, k_cache, v_cache and slot_mapping are required");
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
