@@ -25,11 +25,13 @@
 //  * masked keys (causal, or past the sequence end) are removed by select, and value
 //    entries past the sequence end are zeroed while staging, so NaN in unwritten slots
 //    cannot leak.
-// Tiles are staged through registers with one tile of prefetch: the loads of tile t+1
-// are in flight while tile t is multiplied, and one barrier per tile separates the two
-// LDS buffers. (Two waves share each SIMD, so one wave's softmax overlaps the other's
-// MFMAs when they drift apart.) LDS tiles are XOR-swizzled in 16-byte units so that the 16-byte operand
-// reads of a half-wave hit distinct banks.
+// Tiles go from global memory straight into LDS (global_load_lds, 16 bytes per lane),
+// double-buffered: the loads of tile t+1 are in flight while tile t is multiplied, and
+// one barrier per tile separates the buffers. Each lane picks the global 16 bytes that
+// belong in its LDS slot, so the tiles land XOR-swizzled in 16-byte units and the
+// 16-byte operand reads of a half-wave hit distinct banks. The compiler does not count
+// these loads as LDS writes, so the kernel waits for them explicitly (vmcnt) before the
+// barrier that publishes a tile.
 //
 // Workgroups take tasks last-first: last sequence, last rows first, kv head fastest.
 // For chunks listed in ascending-context order that starts the longest tiles first.
@@ -44,12 +46,20 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest weight let through unscaled
 constexpr int kTK = 64;              // keys per tile
+// s_waitcnt immediate for gfx9: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ inline bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 // Key row (within a 32-key half tile) that MFMA row m reads; see the header comment.
 __device__ inline int perm_key(int m) {
   return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+// One 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i). Kept out of
+// the kernel template: the builtin only exists for the device compilation.
+__device__ __attribute__((always_inline)) inline void lds_dma16(const uint16_t* src, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
 
 // 16-byte-unit swizzles of the LDS tiles.
@@ -62,19 +72,14 @@ __device__ inline int val_swz(int dim) { return (dim >> 3) & 1; }
 }  // namespace
 
 template <int D, int NW, int NS>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_kernel(AttnParams p) {
   constexpr int CPR = D / 8;                      // 16-byte chunks per key row
-  constexpr int KCH = kTK * CPR;                  // chunks per key tile
-  constexpr int VCH = (kTK / kBlock) * D * 2;     // chunks per value tile
   constexpr int NT = NW * 64;
-  static_assert(KCH % NT == 0 && VCH % NT == 0, "tile must split evenly over the workgroup");
-  constexpr int KPT = KCH / NT;
-  constexpr int VPT = VCH / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kTK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kTK * D];
+  static_assert((16 * D / 64) % NW == 0, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * kTK * D];  // keys, then values
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int lane = tid & 63;
   const int col = lane & 31;  // MFMA column within a strip
   const int h2 = lane >> 5;   // lane half
@@ -141,65 +146,52 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnParams p) {
     for (int md = 0; md < D / 32; ++md) o[s][md] = f32x16{};
   }
 
-  // ---- staging: key tile / value tile of keys [kt, kt + 64) -> registers -> LDS ----
-  u32x4 kreg[KPT], vreg[VPT];
-  auto gather_k = [&](int kt) {
+  // ---- staging: key and value tile of keys [kt, kt + 64), global -> LDS directly ----
+  // The tile is 16*D 16-byte slots: key slots [0, 8D) then value slots [8D, 16D). Each
+  // wave instruction fills 64 consecutive slots (lane i -> slot base + i), so each lane
+  // fetches the global 16 bytes that belong in its slot under the XOR swizzle. All 64
+  // slots of one instruction lie in one block, so the block id is loaded once per wave.
+  // Blocks at or past the sequence end are read from the sequence's first block instead
+  // (any valid memory): their keys are masked and their values zeroed before use.
+  constexpr int kSlots = 16 * D;
+  constexpr int kInstPerWave = kSlots / 64 / NW;
+  // Block ids of a tile: lane l holds the id of the tile's block l (l < 4); loaded one
+  // tile ahead so that the barrier's wait covers them.
+  auto load_ids = [&](int kt) {
+    const int b = (kt >> 4) + (lane & 3);
+    return (b * kBlock < L) ? bt[b] : bt[0];
+  };
+  auto dma = [&](int buf, int ids) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int ci = tid + NT * j;
-      const int row = ci / CPR;
-      // A block holds 16 * CPR chunks, a multiple of 64, and a wave's 64 chunk indices
-      // are 64-aligned: all lanes of a wave stage the same block, so its id is loaded
-      // once per wave (scalar).
-      const int b = __builtin_amdgcn_readfirstlane((kt + row) >> 4);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (b * kBlock < L) {
-        const int64_t phys = bt[b];
-        w = *reinterpret_cast<const u32x4*>(kc + ((phys * hkv + g) * kBlock + (row & 15)) * D + (ci % CPR) * 8);
+    for (int j = 0; j < kInstPerWave; ++j) {
+      const int gi = wave * kInstPerWave + j;
+      const int s = gi * 64 + lane;
+      const uint16_t* srcp;
+      if (gi * 64 < 8 * D) {
+        const int row = s / CPR;
+        const int gc = (s % CPR) ^ key_swz<D>(row);
+        const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 / CPR) >> 4);
+        srcp = kc + ((phys * hkv + g) * kBlock + (row & 15)) * D + gc * 8;
+      } else {
+        const int sv = s - 8 * D;
+        const int dim = (sv >> 1) % D;
+        const int gh = (sv & 1) ^ val_swz(dim);
+        const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 - 8 * D) / (2 * D));
+        srcp = vc + ((phys * hkv + g) * D + dim) * kBlock + gh * 8;
       }
-      kreg[j] = w;
+      lds_dma16(srcp, &lds[buf][gi * 64 * 8]);
     }
   };
-  auto gather_v = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int ci = tid + NT * j;
-      const int bl = ci / (2 * D);
-      const int dim = (ci >> 1) % D;
-      const int half = ci & 1;
-      // 2 * D chunks per block, a multiple of 64: the block is wave-uniform here too.
-      const int b = __builtin_amdgcn_readfirstlane((kt >> 4) + bl);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (b * kBlock < L) {
-        const int64_t phys = bt[b];
-        w = *reinterpret_cast<const u32x4*>(vc + ((phys * hkv + g) * D + dim) * kBlock + half * 8);
-        const int key0 = b * kBlock + half * 8;
-        if (key0 + 8 > L) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
-      }
-      vreg[j] = w;
-    }
-  };
-  auto stage_k = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int ci = tid + NT * j;
-      const int row = ci / CPR;
-      const int c = (ci % CPR) ^ key_swz<D>(row);
-      *reinterpret_cast<u32x4*>(&ks[buf][row * D + c * 8]) = kreg[j];
-    }
-  };
-  auto stage_v = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int ci = tid + NT * j;
-      const int bl = ci / (2 * D);
-      const int dim = (ci >> 1) % D;
-      const int half = (ci & 1) ^ val_swz(dim);
-      *reinterpret_cast<u32x4*>(&vs[buf][(bl * D + dim) * kBlock + half * 8]) = vreg[j];
+  // Zero the value entries of keys [L, kt + 64) in a staged tile (only the tile that
+  // holds the sequence end needs it).
+  auto zero_tail = [&](int kt, int buf) {
+    const int k0 = max(L, kt);
+    const int nk = kt + kTK - k0;
+    for (int x = tid; x < nk * D; x += NT) {
+      const int key = k0 - kt + x / D;
+      const int dim = x % D;
+      const int bl = key >> 4, o = key & 15;
+      lds[buf][8 * D * 8 + (bl * D + dim) * kBlock + (((o >> 3) ^ val_swz(dim)) * 8) + (o & 7)] = 0;
     }
   };
 
@@ -208,8 +200,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) sc[s][0] = sc[s][1] = f32x16{};
     const int row0 = perm_key(col);
-    const uint16_t* kr0 = &ks[buf][row0 * D];
-    const uint16_t* kr1 = &ks[buf][(32 + row0) * D];
+    const uint16_t* kr0 = &lds[buf][row0 * D];
+    const uint16_t* kr1 = &lds[buf][(32 + row0) * D];
     const int sw0 = key_swz<D>(row0), sw1 = key_swz<D>(32 + row0);
 #pragma unroll
     for (int kq = 0; kq < D / 16; ++kq) {
@@ -295,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnParams p) {
       const int sw = val_swz(dim);
 #pragma unroll
       for (int ub = 0; ub < 4; ++ub) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vs[buf][(ub * D + dim) * kBlock + ((h2 ^ sw) * 8)]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds[buf][8 * D * 8 + (ub * D + dim) * kBlock + ((h2 ^ sw) * 8)]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) o[s][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s][ub], o[s][md], 0, 0, 0);
       }
@@ -315,16 +307,22 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnParams p) {
     wtm = min(wtm, (ctx + srow0[s] + 1) / kTK);
   }
 
-  gather_k(0);
-  gather_v(0);
+  dma(0, load_ids(0));
+  int ids_next = kmax > kTK ? load_ids(kTK) : 0;
   int buf = 0;
   for (int kt = 0; kt < kmax; kt += kTK, buf ^= 1) {
-    stage_k(buf);
-    stage_v(buf);
+    // The compiler does not count LDS-DMA loads as LDS writes, so the barrier alone
+    // would not wait for them: wait for every outstanding vector-memory operation of
+    // this wave (this tile's DMA and the next tile's block ids), then publish.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (kt + kTK < kmax) {
-      gather_k(kt + kTK);
-      gather_v(kt + kTK);
+    if (kt + kTK > L) {
+      zero_tail(kt, buf);
+      __syncthreads();
+    }
+    if (kt + kTK < kmax) {  // the other buffer was released by the barrier above
+      dma(buf ^ 1, ids_next);
+      if (kt + 2 * kTK < kmax) ids_next = load_ids(kt + 2 * kTK);
     }
     if (kt >= wkmax) continue;
     f32x16 sc[NS][2];
