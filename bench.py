@@ -175,8 +175,8 @@ def main():
             run_step()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        kernels = {k: timer.read(k) for k in ("slot_mapping", "scatter", "plan", "decode", "reduce", "prefill",
-                                              "attn_f32")}
+        kernels = {k: timer.read(k) for k in ("slot_mapping", "scatter", "plan", "prefix", "decode", "reduce",
+                                              "prefill", "attn_f32")}
     ms_per_step = elapsed * 1e3 / args.steps
     value = T / (ms_per_step / 1e3)
     avg_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kernels.items()}

@@ -147,7 +147,12 @@ pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_s
  * workspace: device memory of at least pa_attention_workspace_size() bytes, 256-byte
  * aligned; its contents on entry do not matter. Calls that share a workspace must
  * not overlap in time.
- * Environment: PA_KV_PARTITION=<tokens> (a multiple of 32 in [32, 65536]) overrides
+ * Decode rows whose sequences all start with the same physical blocks (two or more decode
+ * rows; at least 4 whole blocks, holding only cached tokens of every one of them) have
+ * that shared prefix attended once for all of them together; the result is the same up
+ * to rounding (requests sharing cached prefix blocks: shengyayun.com blog, 关键实现细节
+ * item 2).
+ * Environment: PA_KV_PARTITION=<tokens> (a multiple of 64 in [64, 65536]) overrides
  * the split-KV partition length that decode rows use.
  * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED, PA_E_ALIGN,
  * PA_E_WORKSPACE, PA_E_HIP.
@@ -159,6 +164,22 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache,
                        int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim, int64_t num_blocks, pa_dtype dtype, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * What the on-device planner decided in the last pa_attention call that used this
+ * workspace (bf16 steps; the fp32 path plans nothing and leaves info untouched):
+ *   info[0] = decode (sequence, KV partition) tasks
+ *   info[1] = decode rows (sequences with exactly one query row)
+ *   info[2] = keys of the prefix shared by all decode rows and attended once (0: none)
+ *   info[3] = partitions that shared prefix was cut into
+ * The size arguments must be those of that pa_attention call. info is host memory
+ * (4 int32). The call waits for `stream` to finish, then copies 16 bytes.
+ * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED, PA_E_WORKSPACE, PA_E_HIP.
+ */
+pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, int64_t num_tokens,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 pa_dtype dtype, int32_t* info, void* stream);
 
 /*
  * Measurement support. While enabled, every kernel the library launches is bracketed
@@ -174,7 +195,8 @@ typedef enum pa_kernel_kind {
   PA_KERNEL_REDUCE = 4,
   PA_KERNEL_PREFILL = 5,
   PA_KERNEL_ATTN_F32 = 6,
-  PA_KERNEL_KIND_COUNT = 7
+  PA_KERNEL_PREFIX = 7,
+  PA_KERNEL_KIND_COUNT = 8
 } pa_kernel_kind;
 
 pa_status pa_timing_enable(int enable);

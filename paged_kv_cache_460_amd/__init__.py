@@ -9,6 +9,7 @@ from .ops import (
     KernelTimer,
     PAError,
     attention,
+    attention_plan_info,
     attention_workspace_size,
     build_slot_mapping,
     reshape_and_cache,
@@ -22,6 +23,7 @@ __all__ = [
     "LibraryMissing",
     "PAError",
     "attention",
+    "attention_plan_info",
     "attention_workspace_size",
     "build_slot_mapping",
     "load_library",

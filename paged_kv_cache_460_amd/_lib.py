@@ -30,6 +30,7 @@ KERNEL_KINDS = {
     "reduce": 4,
     "prefill": 5,
     "attn_f32": 6,
+    "prefix": 7,
 }
 
 # name -> (restype, argtypes)
@@ -46,6 +47,8 @@ _SIGNATURES = {
                                                    ctypes.POINTER(ctypes.c_size_t)]),
     "pa_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I64, _I32,
                                     _I32, _I32, _I64, ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "pa_attention_plan_info": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                              ctypes.POINTER(_I32), _P]),
     "pa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "pa_timing_reset": (ctypes.c_int, []),
     "pa_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),

@@ -87,16 +87,21 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
   const int64_t wg = blockIdx.x;
   const int g = (int)(wg % hkv);
   const int64_t t = wg / hkv;
-  if (t >= *p.dec_count) return;
+  if (t >= p.plan_hdr[kHdrDecTasks]) return;
   const int task = p.dec_tasks[t];
   const int part = task % p.max_parts;
   const int i = task / p.max_parts;
   const int row = p.qsl[i];
   const int L = p.seq_lens[i];
   const int P = p.part_tokens;
-  const int kbeg = part * P;
+  // With a shared prefix the decode kernel covers only the suffix [prefix_keys, L); the
+  // prefix partials occupy the first prefix_parts slots of the sequence.
+  const int prefix_keys = p.plan_hdr[kHdrPrefixKeys];
+  const int prefix_parts = p.plan_hdr[kHdrPrefixParts];
+  const int kbeg = prefix_keys + part * P;
   const int kend = min(L, kbeg + P);
-  const int nparts = (L + P - 1) / P;
+  const int nparts = prefix_parts + (L - prefix_keys + P - 1) / P;
+  const int slot_part = prefix_parts + part;
   const int G = p.group;
   const int hq = p.num_q_heads;
 
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
       *reinterpret_cast<u32x2*>(orow + dt * 16) = w;
     }
   } else {
-    const int64_t slot = ((int64_t)i * p.max_parts + part) * hq + h;
+    const int64_t slot = ((int64_t)i * p.max_parts + slot_part) * hq + h;
     float* po = p.part_o + slot * D + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt];

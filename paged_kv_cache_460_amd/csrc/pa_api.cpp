@@ -94,7 +94,7 @@ namespace pa {
 int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads) {
   if (const char* env = std::getenv("PA_KV_PARTITION")) {
     const long v = std::strtol(env, nullptr, 10);
-    if (v >= 32 && v <= 65536 && v % 32 == 0) return (int32_t)v;
+    if (v >= 64 && v <= 65536 && v % 64 == 0) return (int32_t)v;
   }
   // One wave streams one (sequence, partition, kv head); waves share HBM, so a long
   // partition is a slow task and the last tasks set the tail. Aim for about eight
@@ -117,18 +117,19 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t n
   size_t off = 0;
   w.tile_offsets = off;
   off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
-  const int64_t max_parts = ((int64_t)max_blocks * kBlock + part_tokens - 1) / part_tokens;
-  w.dec_count = off;
-  off += 256;
+  w.plan_hdr = off;
+  off += align256(sizeof(int32_t) * kHdrSize);
+  // one extra slot per sequence: a shared prefix can split a partition in two
+  const int64_t max_parts = ((int64_t)max_blocks * kBlock + part_tokens - 1) / part_tokens + 1;
   w.dec_tasks = off;
   off += align256(sizeof(int32_t) * (size_t)num_seqs * (size_t)max_parts);
-  if (max_parts > 1) {
-    const size_t slots = (size_t)num_seqs * (size_t)max_parts * (size_t)num_q_heads;
-    w.part_o = off;
-    off += align256(slots * (size_t)head_dim * sizeof(float));
-    w.part_ml = off;
-    off += align256(slots * 2 * sizeof(float));
-  }
+  w.dec_seqs = off;
+  off += align256(sizeof(int32_t) * (size_t)num_seqs);
+  const size_t slots = (size_t)num_seqs * (size_t)max_parts * (size_t)num_q_heads;
+  w.part_o = off;
+  off += align256(slots * (size_t)head_dim * sizeof(float));
+  w.part_ml = off;
+  off += align256(slots * 2 * sizeof(float));
   w.total = off;
   return w;
 }
@@ -267,7 +268,7 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   }
 
   p.part_tokens = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
-  p.max_parts = (int32_t)(((int64_t)max_blocks_per_seq * pa::kBlock + p.part_tokens - 1) / p.part_tokens);
+  p.max_parts = (int32_t)(((int64_t)max_blocks_per_seq * pa::kBlock + p.part_tokens - 1) / p.part_tokens + 1);
   const int64_t decode_grid = (int64_t)num_seqs * p.max_parts * num_kv_heads;
   if (decode_grid > INT32_MAX || (int64_t)num_seqs * p.max_parts > INT32_MAX)
     return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)decode_grid);
@@ -279,21 +280,44 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   if (!aligned16(workspace)) return fail(PA_E_ALIGN, "workspace must be 16-byte aligned");
   char* base = static_cast<char*>(workspace);
   p.tile_offsets = reinterpret_cast<int32_t*>(base + w.tile_offsets);
+  p.plan_hdr = reinterpret_cast<int32_t*>(base + w.plan_hdr);
   p.dec_tasks = reinterpret_cast<int32_t*>(base + w.dec_tasks);
-  p.dec_count = reinterpret_cast<int32_t*>(base + w.dec_count);
-  p.part_o = p.max_parts > 1 ? reinterpret_cast<float*>(base + w.part_o) : nullptr;
-  p.part_ml = p.max_parts > 1 ? reinterpret_cast<float*>(base + w.part_ml) : nullptr;
+  p.dec_seqs = reinterpret_cast<int32_t*>(base + w.dec_seqs);
+  p.part_o = reinterpret_cast<float*>(base + w.part_o);
+  p.part_ml = reinterpret_cast<float*>(base + w.part_ml);
 
   hipError_t e = timed(PA_KERNEL_PLAN, s, [&] { return pa::launch_plan(p, s); });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
+  e = timed(PA_KERNEL_PREFIX, s, [&] { return pa::launch_prefix_bf16(p, s); });
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix launch");
   e = timed(PA_KERNEL_DECODE, s, [&] { return pa::launch_decode_bf16(p, s); });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (p.max_parts > 1) {
-    e = timed(PA_KERNEL_REDUCE, s, [&] { return pa::launch_reduce(p, s); });
-    if (e != hipSuccess) return hip_fail(e, "reduce launch");
-  }
+  e = timed(PA_KERNEL_REDUCE, s, [&] { return pa::launch_reduce(p, s); });
+  if (e != hipSuccess) return hip_fail(e, "reduce launch");
   e = timed(PA_KERNEL_PREFILL, s, [&] { return pa::launch_prefill_bf16(p, s); });
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return PA_OK;
+}
+
+pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, int64_t num_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype, int32_t* info,
+                                 void* stream) {
+  if (!info) return fail(PA_E_NULL, "info is required");
+  const pa_status st = check_attention_sizes(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads,
+                                             head_dim, dtype);
+  if (st != PA_OK) return st;
+  if (dtype != PA_BF16 || num_seqs == 0 || num_tokens == 0) return PA_OK;  // nothing planned
+  const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_q_heads, head_dim, dtype, P);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, workspace_bytes);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess)
+    e = hipMemcpy(info, static_cast<const char*>(workspace) + w.plan_hdr, sizeof(int32_t) * pa::kHdrSize,
+                  hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the plan");
   return PA_OK;
 }
 

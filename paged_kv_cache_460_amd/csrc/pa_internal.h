@@ -42,21 +42,31 @@ struct AttnParams {
   int64_t num_blocks;
   float scale;
   // split-KV decode
-  int32_t part_tokens;   // partition length P (multiple of 32)
-  int32_t max_parts;     // ceil(MB * 16 / P)
+  int32_t part_tokens;   // partition length P (multiple of 64)
+  int32_t max_parts;     // partial slots per sequence: ceil(MB * 16 / P) + 1 (a shared
+                         // prefix can split one partition in two)
   float* part_o;         // [S, max_parts, Hq, D] unnormalised partial outputs
   float* part_ml;        // [S, max_parts, Hq, 2]  running max (log2 domain) and sum
-  // prefill work list
+  // work lists written by the planner
   int32_t* tile_offsets; // [S + 1] exclusive prefix of prefill tiles per sequence
   int32_t* dec_tasks;    // [S * max_parts] decode tasks, sequence * max_parts + partition
-  int32_t* dec_count;    // [1] number of decode tasks
+  int32_t* dec_seqs;     // [S] decode sequences in step order
+  int32_t* plan_hdr;     // [kHdrSize] counts and the shared prefix, see kHdr*
 };
+
+// plan_hdr fields
+constexpr int kHdrDecTasks = 0;     // decode tasks in dec_tasks
+constexpr int kHdrDecSeqs = 1;      // decode sequences in dec_seqs
+constexpr int kHdrPrefixKeys = 2;   // keys of the shared prefix (0: none)
+constexpr int kHdrPrefixParts = 3;  // partitions the shared prefix is cut into
+constexpr int kHdrSize = 4;
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WorkspaceLayout {
   size_t tile_offsets;
+  size_t plan_hdr;
   size_t dec_tasks;
-  size_t dec_count;
+  size_t dec_seqs;
   size_t part_o;
   size_t part_ml;
   size_t total;
@@ -77,6 +87,7 @@ hipError_t launch_plan(const AttnParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_reduce(const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_prefix_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 
 // --- small device helpers ---------------------------------------------------

@@ -71,7 +71,7 @@ __device__ inline int val_swz(int dim) { return (dim >> 3) & 1; }
 
 }  // namespace
 
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, bool kPrefix>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_kernel(AttnParams p) {
   constexpr int CPR = D / 8;                      // 16-byte chunks per key row
   constexpr int NT = NW * 64;
@@ -86,24 +86,51 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int G = p.group;
   const int hkv = p.num_kv_heads;
   const int hq = p.num_q_heads;
-  const int RW = 32 / G;
+  const int RW = 32 / G;      // query rows (chunk mode) or decode sequences (prefix mode) per strip
   const int R = NW * NS * RW;
-  const int S = p.num_seqs;
-  const int total_tiles = p.tile_offsets[S];
   const int64_t u = blockIdx.x;
-  if (u >= (int64_t)total_tiles * hkv) return;
 
-  const int g = (int)(u % hkv);
-  const int tile = total_tiles - 1 - (int)(u / hkv);
-  const int i = upper_index(p.tile_offsets, S, tile);
-  const int rt = tile - p.tile_offsets[i];
-  const int q0 = p.qsl[i];
-  const int n = p.qsl[i + 1] - q0;
-  const int ctx = p.ctx[i];
-  const int L = p.seq_lens[i];
-  const int r0 = rt * R;
-  const int kmax = ctx + min(r0 + R, n);  // keys [0, kmax) are seen by some row of the tile
-  const int32_t* __restrict__ bt = p.block_tables + (int64_t)i * p.max_blocks;
+  // ---- the task: which keys, which block table, which query columns ----
+  // Chunk mode: (chunk sequence, tile of R rows, kv head); rows attend causally to keys
+  //   [0, ctx + row]. Prefix mode: (shared-prefix partition, tile of R decode sequences,
+  //   kv head); every decode row sees every key of the shared prefix, and the result is
+  //   a partial (o, m, l) for the merge kernel.
+  int g, kbeg, kmax, L, seq_or_pp;
+  const int32_t* __restrict__ bt;
+  int q0 = 0, n = 0, ctx = 0, r0 = 0, ct = 0, nds = 0;
+  if constexpr (kPrefix) {
+    const int pkeys = p.plan_hdr[kHdrPrefixKeys];
+    if (pkeys == 0) return;
+    nds = p.plan_hdr[kHdrDecSeqs];
+    const int n_ct = (nds + R - 1) / R;
+    if (u >= (int64_t)p.plan_hdr[kHdrPrefixParts] * n_ct * hkv) return;
+    g = (int)(u % hkv);
+    const int rest = (int)(u / hkv);
+    ct = rest % n_ct;
+    const int pp = rest / n_ct;
+    kbeg = pp * p.part_tokens;
+    kmax = min(pkeys, kbeg + p.part_tokens);
+    L = pkeys;  // keys at or past the shared prefix are masked (they are not shared)
+    seq_or_pp = pp;
+    bt = p.block_tables + (int64_t)p.dec_seqs[0] * p.max_blocks;
+  } else {
+    const int S = p.num_seqs;
+    const int total_tiles = p.tile_offsets[S];
+    if (u >= (int64_t)total_tiles * hkv) return;
+    g = (int)(u % hkv);
+    const int tile = total_tiles - 1 - (int)(u / hkv);
+    const int i = upper_index(p.tile_offsets, S, tile);
+    const int rt = tile - p.tile_offsets[i];
+    q0 = p.qsl[i];
+    n = p.qsl[i + 1] - q0;
+    ctx = p.ctx[i];
+    L = p.seq_lens[i];
+    r0 = rt * R;
+    kbeg = 0;
+    kmax = ctx + min(r0 + R, n);  // keys [0, kmax) are seen by some row of the tile
+    seq_or_pp = i;
+    bt = p.block_tables + (int64_t)i * p.max_blocks;
+  }
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(p.k_cache);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(p.v_cache);
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
@@ -113,21 +140,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // (floored at a tiny positive value so that masked -inf scores still map to weight 0)
   const float sl2 = fmaxf(fabsf(p.scale) * kLog2e, 1e-30f);
 
-  // ---- per strip: rows, validity, query operands ----
-  int srow0[NS], skmax[NS], cpos[NS], crow[NS];
+  // ---- per strip: columns, validity, query operands ----
+  // srow0: first row (chunk) or first decode-sequence index (prefix) of the strip;
+  // crow: this column's row / decode-sequence index; cpos: last key the column sees.
+  int srow0[NS], skmax[NS], cpos[NS], crow[NS], qrow[NS];
   bool cvalid[NS];
   bf16x8 qf[NS][D / 16];
   const int head = g * G + (col % G);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    srow0[s] = r0 + (wave * NS + s) * RW;
-    const int srows = max(0, min(RW, n - srow0[s]));
-    skmax[s] = srows > 0 ? ctx + srow0[s] + srows : 0;
-    crow[s] = srow0[s] + col / G;
-    cvalid[s] = (col < RW * G) && (crow[s] < n);
-    // Idle columns mirror the strip's first row so their arithmetic stays finite.
-    cpos[s] = cvalid[s] ? ctx + crow[s] : ctx + srow0[s];
-    const uint16_t* qr = qg + ((int64_t)(q0 + (cvalid[s] ? crow[s] : min(srow0[s], n - 1))) * hq + head) * D + h2 * 8;
+    if constexpr (kPrefix) {
+      srow0[s] = ct * R + (wave * NS + s) * RW;
+      crow[s] = srow0[s] + col / G;
+      cvalid[s] = (col < RW * G) && (crow[s] < nds);
+      skmax[s] = srow0[s] < nds ? kmax : 0;
+      cpos[s] = L - 1;
+      qrow[s] = p.qsl[p.dec_seqs[cvalid[s] ? crow[s] : 0]];
+    } else {
+      srow0[s] = r0 + (wave * NS + s) * RW;
+      const int srows = max(0, min(RW, n - srow0[s]));
+      skmax[s] = srows > 0 ? ctx + srow0[s] + srows : 0;
+      crow[s] = srow0[s] + col / G;
+      cvalid[s] = (col < RW * G) && (crow[s] < n);
+      // Idle columns mirror the strip's first row so their arithmetic stays finite.
+      cpos[s] = cvalid[s] ? ctx + crow[s] : ctx + srow0[s];
+      qrow[s] = q0 + (cvalid[s] ? crow[s] : min(srow0[s], n - 1));
+    }
+    const uint16_t* qr = qg + ((int64_t)qrow[s] * hq + head) * D + h2 * 8;
 #pragma unroll
     for (int kq = 0; kq < D / 16; ++kq) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qr + kq * 16);
@@ -299,18 +338,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // LDS buffers alternate and one barrier per tile separates them. Waves whose rows need
   // no more keys skip the arithmetic but keep staging and meeting the barrier.
   int wkmax = 0;  // keys this wave's strips need
-  int wtm = 1 << 30;  // first tile that needs the causal mask
+  int wtm = 1 << 30;  // first tile that needs the mask
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     wkmax = max(wkmax, skmax[s]);
-    // tile t holds keys up to 64t + 63; the strip's first row sits at ctx + srow0
-    wtm = min(wtm, (ctx + srow0[s] + 1) / kTK);
+    // tile t holds keys up to 64t + 63; the strip's earliest column sees keys up to
+    // ctx + srow0 (chunk) or the whole prefix (prefix)
+    wtm = min(wtm, ((kPrefix ? L - 1 : ctx + srow0[s]) + 1) / kTK);
   }
 
-  dma(0, load_ids(0));
-  int ids_next = kmax > kTK ? load_ids(kTK) : 0;
+  dma(0, load_ids(kbeg));
+  int ids_next = kbeg + kTK < kmax ? load_ids(kbeg + kTK) : 0;
   int buf = 0;
-  for (int kt = 0; kt < kmax; kt += kTK, buf ^= 1) {
+  for (int kt = kbeg; kt < kmax; kt += kTK, buf ^= 1) {
     // The compiler does not count LDS-DMA loads as LDS writes, so the barrier alone
     // would not wait for them: wait for every outstanding vector-memory operation of
     // this wave (this tile's DMA and the next tile's block ids), then publish.
@@ -335,13 +375,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     pv(buf, pf);
   }
 
-  // ---- epilogue: normalise, round to bf16, write this lane's 4 x 4 dims per 32 ----
+  // ---- epilogue ----
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const float lt = l[s] + __shfl_xor(l[s], 32);
     if (!cvalid[s]) continue;
+    if constexpr (kPrefix) {
+      // partial of shared-prefix partition seq_or_pp for decode sequence dec_seqs[crow]:
+      // unnormalised o, running max and weight sum (the merge kernel finishes the row)
+      const int64_t slot = ((int64_t)p.dec_seqs[crow[s]] * p.max_parts + seq_or_pp) * hq + head;
+      float* po = p.part_o + slot * D + 4 * h2;
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp)
+          *reinterpret_cast<f32x4*>(po + md * 32 + grp * 8) =
+              f32x4{o[s][md][grp * 4 + 0], o[s][md][grp * 4 + 1], o[s][md][grp * 4 + 2], o[s][md][grp * 4 + 3]};
+      if (h2 == 0) {
+        p.part_ml[slot * 2 + 0] = m[s];
+        p.part_ml[slot * 2 + 1] = lt;
+      }
+      continue;
+    }
+    // normalise, round to bf16, write this lane's 4 x 4 dims per 32
     const float inv = 1.0f / lt;
-    uint16_t* orow = og + ((int64_t)(q0 + crow[s]) * hq + head) * D + 4 * h2;
+    uint16_t* orow = og + ((int64_t)qrow[s] * hq + head) * D + 4 * h2;
 #pragma unroll
     for (int md = 0; md < D / 32; ++md) {
 #pragma unroll
@@ -368,10 +426,28 @@ hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream) {
   const int64_t tiles = (p.num_tokens + (int64_t)(R - 1) * chunks) / R + 1;
   const int64_t grid = tiles * p.num_kv_heads;
   if (p.head_dim == 128) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillWaves, kPrefillStrips>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillWaves, kPrefillStrips, false>), dim3((unsigned)grid),
                        dim3(kPrefillWaves * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, kPrefillWaves, kPrefillStrips>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, kPrefillWaves, kPrefillStrips, false>), dim3((unsigned)grid),
+                       dim3(kPrefillWaves * 64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_bf16(const AttnParams& p, hipStream_t stream) {
+  if (p.num_seqs < 2) return hipSuccess;
+  // Upper bound on the planner's shared-prefix tasks: a prefix of at most max_parts - 1
+  // partitions (it leaves every decode sequence at least its new token), R decode
+  // sequences per column tile. Workgroups past the planned tasks exit at once.
+  const int R = prefill_rows_per_tile(p.group);
+  const int64_t col_tiles = (p.num_seqs + R - 1) / R;
+  const int64_t grid = (int64_t)std::max(1, p.max_parts - 1) * col_tiles * p.num_kv_heads;
+  if (p.head_dim == 128) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillWaves, kPrefillStrips, true>), dim3((unsigned)grid),
+                       dim3(kPrefillWaves * 64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, kPrefillWaves, kPrefillStrips, true>), dim3((unsigned)grid),
                        dim3(kPrefillWaves * 64), 0, stream, p);
   }
   return hipGetLastError();

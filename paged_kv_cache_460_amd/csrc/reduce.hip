@@ -1,7 +1,8 @@
 // Merge of split-KV decode partials.
 //
 // Each partition p of a decode row left an unnormalised output o_p, its running max m_p
-// (log2 domain) and its weight sum l_p. Softmax over the union of the partitions is
+// (log2 domain) and its weight sum l_p: the shared-prefix partitions (prefill kernel,
+// prefix mode) first, then the suffix partitions (decode kernel). Softmax over the union of the partitions is
 //   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p,
 // an exact rewrite of the single-pass sum; the result is rounded once to bf16.
 // One wave per (sequence, query head): lanes take partitions for the max and the
@@ -22,7 +23,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnParams p) {
   const int row = p.qsl[i];
   if (p.qsl[i + 1] - row != 1) return;
   const int P = p.part_tokens;
-  const int nparts = (p.seq_lens[i] + P - 1) / P;
+  const int prefix_keys = p.plan_hdr[kHdrPrefixKeys];
+  const int nparts = p.plan_hdr[kHdrPrefixParts] + (p.seq_lens[i] - prefix_keys + P - 1) / P;
   if (nparts <= 1) return;
   const int64_t base = (int64_t)i * p.max_parts * hq + h;  // slot of partition 0; stride hq
 
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnParams p) {
 
 hipError_t launch_reduce(const AttnParams& p, hipStream_t stream) {
   const int64_t items = (int64_t)p.num_seqs * p.num_q_heads;
-  if (items == 0 || p.max_parts <= 1) return hipSuccess;
+  if (items == 0) return hipSuccess;
   const int64_t grid = (items + 3) / 4;
   if (p.head_dim == 128) {
     hipLaunchKernelGGL(reduce_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, p);

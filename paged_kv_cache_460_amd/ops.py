@@ -156,6 +156,21 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cont
     return out
 
 
+def attention_plan_info(workspace, q, k_cache, block_tables):
+    """The on-device planner's summary of the last ``attention`` call that used
+    ``workspace`` with these tensors' sizes (see pa_attention_plan_info in pa.h)."""
+    lib = _lib.load()
+    _need(workspace, "workspace", torch.uint8, 1)
+    T, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    S, MB = block_tables.shape
+    info = (ctypes.c_int32 * 4)()
+    _check(lib.pa_attention_plan_info(_ptr(workspace), workspace.numel(), S, MB, T, hq, hkv, d,
+                                      _payload_dtype(q, "q"), info, _stream(q)))
+    return {"decode_tasks": info[0], "decode_rows": info[1], "shared_prefix_keys": info[2],
+            "shared_prefix_parts": info[3]}
+
+
 def step(q, k, v, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out=None,
          workspace=None, slot_mapping=None):
     """One whole step on the current stream: slot mapping, cache write, attention."""

@@ -103,6 +103,24 @@ def test_workspace_size(lib):
     assert out.value >= bf16
 
 
+def test_plan_info_validation(lib):
+    info = (ctypes.c_int32 * 4)(7, 7, 7, 7)
+
+    def call(ws=A, nbytes=1 << 40, S=4, MB=4, T=4, hq=4, hkv=1, d=64, dt=1, out=info):
+        return lib.pa_attention_plan_info(ws, nbytes, S, MB, T, hq, hkv, d, dt, out, P(0))
+
+    assert call(out=None) == E_NULL
+    assert call(dt=5) == E_DTYPE
+    assert call(d=96) == E_UNSUP
+    assert call(hq=6, hkv=4) == E_SHAPE
+    assert call(ws=P(0)) == E_WS
+    assert call(nbytes=16) == E_WS
+    # fp32 steps and empty steps plan nothing: OK without touching the device or info
+    assert call(dt=0) == OK
+    assert call(S=0, T=0) == OK
+    assert list(info) == [7, 7, 7, 7]
+
+
 def test_reshape_and_cache_validation(lib):
     def call(k=A, v=A, kc=A, vc=A, sm=A, T=4, hkv=2, d=128, nb=8, dt=1):
         return lib.pa_reshape_and_cache(k, v, kc, vc, sm, T, hkv, d, nb, dt, P(0))
