@@ -30,39 +30,51 @@ namespace {
 constexpr int kBuckets = 32;
 constexpr int kMinPrefixBlocks = 4;  // shorter shared runs are left to the decode kernel
 
-__device__ inline int block_exclusive_scan(int32_t* sums, int tid, int value, int& total) {
-  sums[tid] = value;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = tid >= off ? sums[tid - off] : 0;
-    __syncthreads();
-    sums[tid] += add;
-    __syncthreads();
+// Block-wide exclusive scan and minimum for the 1024-thread planner: within each wave by
+// cross-lane shuffles, then over the 16 wave results through LDS (two barriers each).
+__device__ inline int block_exclusive_scan(int32_t* wsum, int tid, int value, int& total) {
+  const int lane = tid & 63, w = tid >> 6;
+  int v = value;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
   }
-  total = sums[1023];
-  const int excl = sums[tid] - value;
+  if (lane == 63) wsum[w] = v;
   __syncthreads();
-  return excl;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int x = wsum[k];
+    before += k < w ? x : 0;
+    all += x;
+  }
+  __syncthreads();  // wsum may be reused by the next call
+  total = all;
+  return before + v - value;
 }
 
-__device__ inline int block_min(int32_t* sums, int tid, int value) {
-  sums[tid] = value;
+__device__ inline int block_min(int32_t* wsum, int tid, int value) {
+  const int lane = tid & 63, w = tid >> 6;
+  int v = value;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
+  if (lane == 0) wsum[w] = v;
   __syncthreads();
-  for (int off = 512; off > 0; off >>= 1) {
-    if (tid < off) sums[tid] = min(sums[tid], sums[tid + off]);
-    __syncthreads();
-  }
-  const int r = sums[0];
+  int r = wsum[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) r = min(r, wsum[k]);
   __syncthreads();
   return r;
 }
 }  // namespace
 
 __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_per_tile) {
-  __shared__ int32_t sums[1024];
+  __shared__ int32_t sums[16];  // per-wave partial results of the block reductions
   __shared__ int32_t bcount[kBuckets];
   __shared__ int32_t bfill[kBuckets];
   __shared__ int32_t boff[kBuckets];
+  __shared__ int32_t mismatch;
   const int32_t* __restrict__ qsl = p.qsl;
   const int32_t* __restrict__ seq_lens = p.seq_lens;
   const int num_seqs = p.num_seqs;
@@ -96,8 +108,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   if (tid == 0) p.tile_offsets[num_seqs] = total_tiles;
 
   // ---- shared prefix: common leading blocks of every decode sequence ----
-  // The first decode sequence is the reference (found by a block-wide min, not read
-  // back from dec_seqs).
+  // The first decode sequence is the reference (found by a block-wide min). Cheap test
+  // first: every decode sequence must hold a cached block 0 equal to the reference's;
+  // only then are all (sequence, block) pairs up to the shortest cached run compared,
+  // in parallel, for the first mismatch.
   int my_first = 1 << 30;
   for (int i = b; i < e; ++i)
     if (qsl[i + 1] - qsl[i] == 1) {
@@ -105,19 +119,31 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
       break;
     }
   const int ref = block_min(sums, tid, my_first);
-  int lcp = 1 << 30;
+  int prefix_blocks = 0;
   if (total_dec >= 2) {
     const int32_t* __restrict__ bref = p.block_tables + (int64_t)ref * MB;
+    int cap_local = 1 << 30, same_first = 1;
     for (int i = b; i < e; ++i) {
       if (qsl[i + 1] - qsl[i] != 1) continue;
       const int cap = (seq_lens[i] - 1) / kBlock;  // blocks holding only cached tokens
-      const int32_t* __restrict__ bi = p.block_tables + (int64_t)i * MB;
-      int c = 0;
-      while (c < cap && bi[c] == bref[c]) ++c;
-      lcp = min(lcp, c);
+      cap_local = min(cap_local, cap);
+      if (cap == 0 || p.block_tables[(int64_t)i * MB] != bref[0]) same_first = 0;
+    }
+    const int cap = block_min(sums, tid, cap_local);
+    const int all_same_first = block_min(sums, tid, same_first);
+    if (all_same_first && cap >= kMinPrefixBlocks) {
+      if (tid == 0) mismatch = cap;
+      __syncthreads();
+      const int64_t pairs = (int64_t)num_seqs * cap;
+      for (int64_t k = tid; k < pairs; k += 1024) {
+        const int i = (int)(k / cap);
+        const int c = (int)(k % cap);
+        if (qsl[i + 1] - qsl[i] == 1 && p.block_tables[(int64_t)i * MB + c] != bref[c]) atomicMin(&mismatch, c);
+      }
+      __syncthreads();
+      prefix_blocks = mismatch;
     }
   }
-  int prefix_blocks = total_dec >= 2 ? block_min(sums, tid, lcp) : 0;
   if (prefix_blocks < kMinPrefixBlocks) prefix_blocks = 0;
   const int prefix_keys = prefix_blocks * kBlock;
 
