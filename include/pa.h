@@ -147,6 +147,10 @@ pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_s
  * workspace: device memory of at least pa_attention_workspace_size() bytes, 256-byte
  * aligned; its contents on entry do not matter. Calls that share a workspace must
  * not overlap in time.
+ * Routing (decided on the device, same results either way): a sequence with one row is a
+ * decode row (split-KV decode); a sequence with 2..16/G rows (speculative-decoding
+ * verification) also takes the split-KV decode path, its rows side by side with per-row
+ * causal limits; a longer sequence is a prefill chunk (MFMA tiles).
  * Decode rows whose sequences all start with the same physical blocks (two or more decode
  * rows; at least 4 whole blocks, holding only cached tokens of every one of them) have
  * that shared prefix attended once for all of them together; the result is the same up

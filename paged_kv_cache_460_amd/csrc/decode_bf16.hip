@@ -94,16 +94,26 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
   const int row = p.qsl[i];
   const int L = p.seq_lens[i];
   const int P = p.part_tokens;
-  // With a shared prefix the decode kernel covers only the suffix [prefix_keys, L); the
-  // prefix partials occupy the first prefix_parts slots of the sequence.
-  const int prefix_keys = p.plan_hdr[kHdrPrefixKeys];
-  const int prefix_parts = p.plan_hdr[kHdrPrefixParts];
+  const int G = p.group;
+  const int hq = p.num_q_heads;
+  // A task is one KV partition of a decode row or of a short multi-row sequence
+  // (speculative-decoding verification: 2..16/G rows), whose (row, head) pairs fill the
+  // MFMA columns. With a shared prefix a decode row covers only the suffix
+  // [prefix_keys, L); the prefix partials occupy its first prefix_parts slots.
+  const int nrows = p.qsl[i + 1] - row;
+  const bool multi = nrows > 1;
+  const int prefix_keys = multi ? 0 : p.plan_hdr[kHdrPrefixKeys];
+  const int prefix_parts = multi ? 0 : p.plan_hdr[kHdrPrefixParts];
   const int kbeg = prefix_keys + part * P;
   const int kend = min(L, kbeg + P);
   const int nparts = prefix_parts + (L - prefix_keys + P - 1) / P;
   const int slot_part = prefix_parts + part;
-  const int G = p.group;
-  const int hq = p.num_q_heads;
+  // column c = (row r, head-in-group hh); row r sits at position L - nrows + r and sees
+  // keys up to it (causal), so its keys stop at climit
+  const int cr = c / G, chh = c % G;
+  const bool cvalid = c < nrows * G;
+  const int climit = cvalid ? min(kend, L - nrows + cr + 1) : kend;
+  const int kmask = min(kend, L - nrows + 1);  // first key some column must not see
 
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(p.k_cache);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(p.v_cache);
@@ -112,11 +122,12 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
   // B operand Q^T: column c, dims kk*32 + qd*8 .. +8.
   bf16x8 qb[D / 32];
   {
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((int64_t)row * hq + g * G + min(c, G - 1)) * D + qd * 8;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)(row + (cvalid ? cr : 0)) * hq + g * G + (cvalid ? chh : 0)) * D + qd * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + kk * 32);
-      qb[kk] = (c < G) ? x : bf16x8{};
+      qb[kk] = cvalid ? x : bf16x8{};
     }
   }
 
@@ -147,16 +158,14 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
       sv[e] = s0[e] * sl2;
       sv[4 + e] = s1[e] * sl2;
     }
-    const bool tail = kb + 2 * kBlock > kend;
+    const bool tail = kb + 2 * kBlock > kmask;
     uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     if (tail) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = kb + (e >> 2) * kBlock + 4 * qd + (e & 3);
-        if (key >= kend) {
-          sv[e] = -INFINITY;
-          vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
+        if (key >= climit) sv[e] = -INFINITY;
+        if (key >= kend) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
     }
     float mx = sv[0];
@@ -165,12 +174,16 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    // A multi-row column can see no key at all in a late partition (its row lies
+    // before the partition): keep its state at m = -inf, l = 0, o = 0 (weight 0 in the
+    // merge) instead of forming -inf - -inf.
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
     float pe[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pe[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
+      pe[e] = __builtin_amdgcn_exp2f(sv[e] - mref);
       psum += pe[e];
     }
     lsum = lsum * alpha + psum;
@@ -195,11 +208,11 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  if (c >= G) return;
-  const int h = g * G + c;
+  if (!cvalid) return;
+  const int h = g * G + chh;
   if (nparts == 1) {
     const float inv = 1.0f / lsum;
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)row * hq + h) * D + qd * 4;
+    uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)(row + cr) * hq + h) * D + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
       *reinterpret_cast<u32x2*>(orow + dt * 16) = w;
     }
   } else {
-    const int64_t slot = ((int64_t)i * p.max_parts + slot_part) * hq + h;
+    const int64_t slot = part_slot(p, i, slot_part, g, c);
     float* po = p.part_o + slot * D + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt];

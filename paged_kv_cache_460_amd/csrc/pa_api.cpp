@@ -110,7 +110,7 @@ int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_he
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_q_heads,
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
                                  int32_t head_dim, pa_dtype dtype, int32_t part_tokens) {
   WorkspaceLayout w{};
   if (dtype != PA_BF16 || num_seqs == 0) return w;  // the fp32 path needs no workspace
@@ -125,7 +125,7 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t n
   off += align256(sizeof(int32_t) * (size_t)num_seqs * (size_t)max_parts);
   w.dec_seqs = off;
   off += align256(sizeof(int32_t) * (size_t)num_seqs);
-  const size_t slots = (size_t)num_seqs * (size_t)max_parts * (size_t)num_q_heads;
+  const size_t slots = (size_t)num_seqs * (size_t)max_parts * (size_t)num_kv_heads * 16;
   w.part_o = off;
   off += align256(slots * (size_t)head_dim * sizeof(float));
   w.part_ml = off;
@@ -221,7 +221,7 @@ pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_s
                                              num_kv_heads, head_dim, dtype);
   if (st != PA_OK) return st;
   const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
-  *bytes = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_q_heads, head_dim, dtype, P).total;
+  *bytes = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype, P).total;
   return PA_OK;
 }
 
@@ -272,7 +272,7 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   const int64_t decode_grid = (int64_t)num_seqs * p.max_parts * num_kv_heads;
   if (decode_grid > INT32_MAX || (int64_t)num_seqs * p.max_parts > INT32_MAX)
     return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)decode_grid);
-  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_q_heads, head_dim, dtype,
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype,
                                                      p.part_tokens);
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", w.total, workspace_bytes,
@@ -309,7 +309,7 @@ pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, 
   if (st != PA_OK) return st;
   if (dtype != PA_BF16 || num_seqs == 0 || num_tokens == 0) return PA_OK;  // nothing planned
   const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
-  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_q_heads, head_dim, dtype, P);
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype, P);
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, workspace_bytes);
   const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -45,14 +45,22 @@ struct AttnParams {
   int32_t part_tokens;   // partition length P (multiple of 64)
   int32_t max_parts;     // partial slots per sequence: ceil(MB * 16 / P) + 1 (a shared
                          // prefix can split one partition in two)
-  float* part_o;         // [S, max_parts, Hq, D] unnormalised partial outputs
-  float* part_ml;        // [S, max_parts, Hq, 2]  running max (log2 domain) and sum
+  float* part_o;         // [S, Hkv, 16, max_parts, D] unnormalised partial outputs
+  float* part_ml;        // [S, Hkv, 16, max_parts, 2] running max (log2 domain) and sum
   // work lists written by the planner
   int32_t* tile_offsets; // [S + 1] exclusive prefix of prefill tiles per sequence
   int32_t* dec_tasks;    // [S * max_parts] decode tasks, sequence * max_parts + partition
   int32_t* dec_seqs;     // [S] decode sequences in step order
   int32_t* plan_hdr;     // [kHdrSize] counts and the shared prefix, see kHdr*
 };
+
+// Partial-result slot of (sequence i, partition q, kv head g, MFMA column c). The 16
+// columns of a kv head hold a partition's (row, head-in-group) pairs, c = row * G + h % G:
+// one row for a decode row, up to 16/G rows for a short multi-row sequence. A column's
+// partitions are adjacent, so the merge reads each column's partials in one run.
+__host__ __device__ inline int64_t part_slot(const AttnParams& p, int i, int q, int g, int c) {
+  return (((int64_t)i * p.num_kv_heads + g) * 16 + c) * p.max_parts + q;
+}
 
 // plan_hdr fields
 constexpr int kHdrDecTasks = 0;     // decode tasks in dec_tasks
@@ -72,7 +80,7 @@ struct WorkspaceLayout {
   size_t total;
 };
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_q_heads,
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
                                  int32_t head_dim, pa_dtype dtype, int32_t part_tokens);
 int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads);
 

@@ -5,7 +5,7 @@
 // blocks for a shared prompt prefix (shengyayun.com blog, 关键实现细节 item 2). All of
 // it is planned on the device from the length arrays and block tables, so a step needs
 // no host round trip:
-//  * chunk sequences (two or more rows) are cut into tiles of prefill_rows_per_tile(G)
+//  * chunk sequences (more than 16/G rows) are cut into tiles of prefill_rows_per_tile(G)
 //    rows; tile_offsets[i] is the exclusive prefix sum of tiles, which lets the prefill
 //    kernel map a flat task index to (sequence, tile);
 //  * decode sequences (one row) are listed in dec_seqs. If all of them (two or more)
@@ -13,6 +13,9 @@
 //    every one of them, the common run of blocks is a shared prefix: it is attended
 //    once for all decode rows together (the prefill kernel's prefix mode) and each
 //    decode sequence keeps only its own suffix;
+//  * sequences of 2..16/G rows (speculative verification) take the decode path as well:
+//    their (row, head) pairs fill the MFMA columns and their whole KV range is cut
+//    into partitions like a decode suffix;
 //  * each decode suffix is cut into KV partitions of P tokens. dec_tasks lists every
 //    (sequence, partition) longest first: all full partitions, then the partial last
 //    partitions in 32 length buckets, longest bucket first. Workgroups are dispatched in
@@ -89,11 +92,17 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   const int P = p.part_tokens;
   const int MB = p.max_blocks;
 
+  // A sequence of 2..16/G rows is a short multi-row step (speculative verification):
+  // the decode kernel takes it, its (row, head) pairs filling the MFMA columns.
+  const int G = p.group;
+  auto is_multi = [&](int n) { return n >= 2 && n * G <= 16; };
+  auto is_chunk = [&](int n) { return n >= 2 && n * G > 16; };
+
   // ---- prefill tiles, decode sequence list ----
   int tiles = 0, ndec = 0;
   for (int i = b; i < e; ++i) {
     const int n = qsl[i + 1] - qsl[i];
-    if (n >= 2) tiles += (n + rows_per_tile - 1) / rows_per_tile;
+    if (is_chunk(n)) tiles += (n + rows_per_tile - 1) / rows_per_tile;
     else if (n == 1) ++ndec;
   }
   int total_tiles, total_dec;
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   for (int i = b; i < e; ++i) {
     p.tile_offsets[i] = tile_run;
     const int n = qsl[i + 1] - qsl[i];
-    if (n >= 2) tile_run += (n + rows_per_tile - 1) / rows_per_tile;
+    if (is_chunk(n)) tile_run += (n + rows_per_tile - 1) / rows_per_tile;
     else if (n == 1) p.dec_seqs[dec_run++] = i;
   }
   if (tid == 0) p.tile_offsets[num_seqs] = total_tiles;
@@ -147,11 +156,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   if (prefix_blocks < kMinPrefixBlocks) prefix_blocks = 0;
   const int prefix_keys = prefix_blocks * kBlock;
 
-  // ---- decode tasks over each suffix [prefix_keys, L) ----
+  // ---- decode-path tasks: partitions of each decode suffix [prefix_keys, L) and of each
+  // multi-row sequence's whole range [0, L) ----
+  auto task_len = [&](int i) {
+    const int n = qsl[i + 1] - qsl[i];
+    return n == 1 ? seq_lens[i] - prefix_keys : (is_multi(n) ? seq_lens[i] : 0);
+  };
   int full = 0;
   for (int i = b; i < e; ++i) {
-    if (qsl[i + 1] - qsl[i] != 1) continue;
-    const int len = seq_lens[i] - prefix_keys;
+    const int len = task_len(i);
     full += len / P;
     if (len % P) atomicAdd(&bcount[(len % P - 1) * kBuckets / P], 1);
   }
@@ -170,8 +183,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   }
   __syncthreads();
   for (int i = b; i < e; ++i) {
-    if (qsl[i + 1] - qsl[i] != 1) continue;
-    const int len = seq_lens[i] - prefix_keys;
+    const int len = task_len(i);
     const int nfull = len / P;
     for (int q = 0; q < nfull; ++q) p.dec_tasks[full_run + q] = i * p.max_parts + q;
     full_run += nfull;

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if constexpr (kPrefix) {
       // partial of shared-prefix partition seq_or_pp for decode sequence dec_seqs[crow]:
       // unnormalised o, running max and weight sum (the merge kernel finishes the row)
-      const int64_t slot = ((int64_t)p.dec_seqs[crow[s]] * p.max_parts + seq_or_pp) * hq + head;
+      const int64_t slot = part_slot(p, p.dec_seqs[crow[s]], seq_or_pp, g, col % G);
       float* po = p.part_o + slot * D + 4 * h2;
 #pragma unroll
       for (int md = 0; md < D / 32; ++md)

@@ -76,6 +76,17 @@ EDGE_CASES = {
     "many_partitions": ([3000, 2047, 4095], [1, 1, 1], 8, 1, 128, "bf16"),
     "f32_mixed_128": ([20, 0, 33], [1, 21, 5], 8, 1, 128, "f32"),
     "f32_mixed_64_gqa": ([0, 70, 5], [9, 1, 2], 6, 3, 64, "f32"),
+    # short multi-row sequences (speculative verification: k+1 rows) take the decode path
+    # while rows x G <= 16; beyond that they are prefill chunks
+    "spec_g4_n4": ([0, 5, 15, 16, 100, 1000], [4, 4, 4, 4, 4, 4], 16, 4, 128, "bf16"),
+    "spec_g8_n2": ([1, 31, 600], [2, 2, 2], 16, 2, 128, "bf16"),
+    "spec_g2_n8": ([0, 9, 77], [8, 3, 8], 4, 2, 128, "bf16"),
+    "spec_g1_n16": ([3, 40, 333], [16, 7, 16], 2, 2, 128, "bf16"),
+    "spec_g4_n5_is_chunk": ([12, 90], [5, 4], 8, 2, 128, "bf16"),
+    "spec_mixed_d64": ([50, 0, 20, 300, 7], [1, 40, 3, 1, 4], 8, 2, 64, "bf16"),
+    # rows on both sides of a 256-token partition boundary: the early rows see no key of
+    # the last partition, whose partial must then carry no weight in the merge
+    "spec_rows_straddle_partition": ([250, 254, 509, 700], [8, 4, 4, 1], 8, 4, 128, "bf16"),
 }
 
 
@@ -179,6 +190,28 @@ def _shared_prefix_step(prefix_blocks, suffix_lens, hq, hkv, d, chunks=(), seed=
     step.block_tables = bt
     # the shared blocks must hold the same data the first sequence sees: they are its blocks
     return step
+
+
+def test_shared_prefix_with_multi_row_sequence():
+    """Decode rows share a prefix with a 3-row sequence: the 3-row sequence reads the
+    prefix itself (the planner's shared set is the single-row decodes only)."""
+    import paged_kv_cache_460_amd as pa
+
+    ctx = [16 * 8 + 5, 16 * 8 + 40, 16 * 8 + 2, 16 * 8 + 9]
+    qlen = [1, 1, 1, 3]
+    step = workload.build_step(ctx, qlen, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16", seed=33,
+                               device=DEV)
+    bt = step.block_tables.clone()
+    bt[1:, :8] = bt[0, :8]
+    step.block_tables = bt
+    check_full(step, "shared_prefix_with_multi_row")
+    kc, vc = step.k_cache.clone(), step.v_cache.clone()
+    ws = torch.empty(pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, step.num_tokens, 16, 4, 128,
+                                                 torch.bfloat16), dtype=torch.uint8, device=DEV)
+    pa.step(step.q, step.k, step.v, kc, vc, step.block_tables, step.seq_lens, step.query_start_loc,
+            step.context_lens, step.scale, workspace=ws)
+    info = pa.attention_plan_info(ws, step.q, kc, step.block_tables)
+    assert info["decode_rows"] == 3 and info["shared_prefix_keys"] == 128, info
 
 
 SHARED_PREFIX_CASES = {

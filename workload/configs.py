@@ -71,12 +71,24 @@ def long_decode_bf16(seed: int = 0, device="cpu", num_seqs: int = 16, seq_len: i
                       seed=seed, device=device, name="long_decode_bf16", **kw)
 
 
+def spec_verify_bf16(seed: int = 0, device="cpu", num_seqs: int = 64, rows: int = 4, lo: int = 512, hi: int = 4096,
+                     max_blocks_per_seq: int = 256, **kw) -> Step:
+    """Speculative-decoding verification step: 64 sequences each verifying 3 drafted tokens
+    (4 query rows: the drafts plus the last accepted token), context ~ U[512, 4096];
+    32/8 heads, D=128. The pages' example drafts 3 tokens per step."""
+    ctx = _lengths_rng(seed).integers(lo, hi, size=num_seqs, endpoint=True)
+    return build_step(ctx, np.full(num_seqs, rows, np.int64), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      dtype="bf16", max_blocks_per_seq=max_blocks_per_seq, seed=seed, device=device,
+                      name="spec_verify_bf16", **kw)
+
+
 CONFIGS = {
     "tiny_decode_f32": tiny_decode_f32,
     "decode_batch_bf16": decode_batch_bf16,
     "mixed_step_bf16": mixed_step_bf16,
     "prefix_shared_bf16": prefix_shared_bf16,
     "long_decode_bf16": long_decode_bf16,
+    "spec_verify_bf16": spec_verify_bf16,
 }
 
 # Reduced sizes with the same structure; the oracle finishes these in seconds.
@@ -87,6 +99,7 @@ SMALL = {
                             max_blocks_per_seq=24),
     "prefix_shared_bf16": dict(num_seqs=5, prefix=64, lo=1, hi=40, max_blocks_per_seq=8),
     "long_decode_bf16": dict(num_seqs=2, seq_len=1500),
+    "spec_verify_bf16": dict(num_seqs=5, lo=0, hi=200, max_blocks_per_seq=16),
 }
 
 
