@@ -1,9 +1,12 @@
 """Throughput of one paged-attention step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu-baseline]
 
 A step is the whole hot path over one synthetic batch: slot mapping, cache write and
-attention over the mixed decode + chunked-prefill super-sequence, on one stream. The
+attention over the mixed decode + chunked-prefill super-sequence, on one stream. By
+default the step is recorded once as a HIP graph and each timed step is one replay
+(--eager: separate launches); per-kernel durations come from a second pass of eager
+steps with HIP events around every launch. The
 default workload is the mixed chunked-prefill step (1664 decode rows plus three
 2048-row prefill chunks with 0 / 2048 / 6144 tokens of cached context; 32 query heads
 over 8 kv heads, head dim 128, bf16, 16-token blocks): the one workload that exercises
@@ -123,6 +126,8 @@ def main():
     ap.add_argument("--workload", default="mixed_step_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as separate launches instead of one HIP-graph replay")
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0 / 3)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many MiB "
@@ -162,25 +167,47 @@ def main():
         pa.attention(step.q, step.k_cache, step.v_cache, step.block_tables, step.seq_lens, step.query_start_loc,
                      step.context_lens, step.scale, out=out, workspace=ws)
 
+    # The step recorded once as a HIP graph (slot mapping, cache write, attention; the
+    # same kernels with the same arguments) and replayed with one launch per step.
+    graph = None if args.eager else pa.StepGraph(step.q, step.k, step.v, step.k_cache, step.v_cache,
+                                                  step.block_tables, step.seq_lens, step.query_start_loc,
+                                                  step.context_lens, step.scale, out, slots, ws)
+    headline = run_step if graph is None else graph.replay
+    mode = "eager" if graph is None else "hip_graph"
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         run_step()
+        if graph is not None:
+            graph.replay()
     torch.cuda.synchronize()
 
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {args.steps} steps ({mode})")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        headline()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = T / (ms_per_step / 1e3)
+    log(f"[bench] {ms_per_step:.3f} ms/step")
+    if graph is not None:
+        graph.close()
+
+    # Per-kernel durations: K eager steps with every launch bracketed by HIP events on its
+    # own stream (libpa's timing); a graph replay runs these same kernels.
+    log(f"[bench] timing {args.steps} eager steps with per-kernel events")
     with pa.KernelTimer() as timer:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             run_step()
         torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+        eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
         kernels = {k: timer.read(k) for k in ("slot_mapping", "scatter", "plan", "prefix", "decode", "reduce",
                                               "prefill", "attn_f32")}
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = T / (ms_per_step / 1e3)
     avg_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kernels.items()}
-    log(f"[bench] {ms_per_step:.3f} ms/step; kernel averages (ms): "
+    log(f"[bench] eager {eager_ms_per_step:.3f} ms/step; kernel averages (ms): "
         + ", ".join(f"{k}={v:.4f}" for k, v in avg_ms.items() if v))
 
     dec_ms = avg_ms["decode"]
@@ -212,6 +239,7 @@ def main():
             "block_size": 16,
             "num_blocks": step.num_blocks,
             "seed": args.seed,
+            "execution": mode,
         },
         "roofline": {
             "bound": "hbm",
@@ -232,6 +260,8 @@ def main():
             "prefill_mfma_util": pre_tflops / BF16_MFMA_PEAK_TFLOPS if pre_tflops else None,
             "prefill_flops_per_launch": work["prefill_flops"],
             "scatter_bytes_per_launch": work["scatter_bytes"],
+            "execution": mode,
+            "eager_ms_per_step_with_kernel_events": eager_ms_per_step,
         },
     }
     if args.copy_probe_mib > 0:

@@ -186,6 +186,45 @@ pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, 
                                  pa_dtype dtype, int32_t* info, void* stream);
 
 /*
+ * Step graphs: one serving step (pa_build_slot_mapping, pa_reshape_and_cache and
+ * pa_attention, in that order) recorded once as a HIP graph and replayed with one launch.
+ * Capturing the step's kernels into a graph, to cut the launch overhead of small steps,
+ * is what the engine does while it warms up (hn.213312.xyz, section 一, engine start-up;
+ * chat-gpts.plus news summary, section 为什么重要).
+ *
+ * pa_step_graph_create takes the arguments of the three calls (same meaning, layouts and
+ * preconditions; positions may be NULL) and records their kernels with these pointers
+ * and sizes; nothing runs at creation. The sizes (num_seqs, max_blocks_per_seq,
+ * num_tokens, heads, head_dim, num_blocks), the scale, the partition length and every
+ * pointer are fixed in the graph. Each replay reads the current contents of the input
+ * buffers (q, k, v, block_tables, seq_lens, query_start_loc, context_lens, the caches),
+ * so a caller refills them in place between replays; a step with fewer rows fits by
+ * padding (rows past query_start_loc[num_seqs] get slot -1 and no output). The graph
+ * writes positions (if given), slot_mapping, the caches, out and the workspace: the
+ * same writes as the three calls, with the same results.
+ * The graph belongs to the device that was current at creation; launch it on a stream
+ * of that device. Replays that share buffers must not overlap in time. Kernel timing
+ * (pa_timing_*) does not see kernels run from a graph.
+ * Creation errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE (also num_seqs, num_tokens or
+ * num_blocks < 1), PA_E_UNSUPPORTED, PA_E_ALIGN, PA_E_WORKSPACE, PA_E_HIP; on error
+ * *graph is NULL and nothing was recorded or launched. pa_step_graph_launch returns
+ * PA_E_NULL for a NULL graph, else PA_E_HIP on a launch error. pa_step_graph_destroy
+ * frees the graph (NULL is a no-op); the caller owns it until then.
+ */
+typedef struct pa_step_graph pa_step_graph;
+
+pa_status pa_step_graph_create(const void* q, const void* k, const void* v, void* k_cache,
+                               void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, const int32_t* context_lens,
+                               float scale, void* out, int32_t* positions, int64_t* slot_mapping,
+                               int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_tokens,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int64_t num_blocks, pa_dtype dtype, void* workspace,
+                               size_t workspace_bytes, pa_step_graph** graph);
+pa_status pa_step_graph_launch(const pa_step_graph* graph, void* stream);
+pa_status pa_step_graph_destroy(pa_step_graph* graph);
+
+/*
  * Measurement support. While enabled, every kernel the library launches is bracketed
  * by HIP events on its stream. pa_timing_read waits for the recorded events and returns
  * the summed duration (ms) and the launch count of one kernel kind since the last reset.

@@ -8,6 +8,7 @@ from ._lib import BLOCK_SIZE, LibraryMissing, LIB_PATH, load as load_library
 from .ops import (
     KernelTimer,
     PAError,
+    StepGraph,
     attention,
     attention_plan_info,
     attention_workspace_size,
@@ -22,6 +23,7 @@ __all__ = [
     "LIB_PATH",
     "LibraryMissing",
     "PAError",
+    "StepGraph",
     "attention",
     "attention_plan_info",
     "attention_workspace_size",

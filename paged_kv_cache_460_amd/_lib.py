@@ -49,6 +49,11 @@ _SIGNATURES = {
                                     _I32, _I32, _I64, ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "pa_attention_plan_info": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
                                               ctypes.POINTER(_I32), _P]),
+    "pa_step_graph_create": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I32,
+                                            _I32, _I64, _I32, _I32, _I32, _I64, ctypes.c_int, _P, ctypes.c_size_t,
+                                            ctypes.POINTER(_P)]),
+    "pa_step_graph_launch": (ctypes.c_int, [_P, _P]),
+    "pa_step_graph_destroy": (ctypes.c_int, [_P]),
     "pa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "pa_timing_reset": (ctypes.c_int, []),
     "pa_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),

@@ -69,11 +69,15 @@ Timing& timing() {
   return t;
 }
 
+// Set while this thread records a step graph: launches are then captured without the
+// timing events (a graph holds kernels only).
+thread_local bool g_capturing = false;
+
 // Launch `fn` (returns hipError_t), bracketed by events when timing is on.
 template <class F>
 hipError_t timed(int kind, hipStream_t stream, F&& fn) {
   Timing& t = timing();
-  if (!t.enabled) return fn();
+  if (!t.enabled || g_capturing) return fn();
   std::lock_guard<std::mutex> lock(t.mu);
   hipEvent_t a = t.take(), b = t.take();
   if (!a || !b) return hipErrorOutOfMemory;
@@ -318,6 +322,97 @@ pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, 
     e = hipMemcpy(info, static_cast<const char*>(workspace) + w.plan_hdr, sizeof(int32_t) * pa::kHdrSize,
                   hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "reading the plan");
+  return PA_OK;
+}
+
+// ---- step graphs ---------------------------------------------------------------
+
+struct pa_step_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+pa_status pa_step_graph_create(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, const int32_t* context_lens, float scale,
+                               void* out, int32_t* positions, int64_t* slot_mapping, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int64_t num_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, pa_dtype dtype,
+                               void* workspace, size_t workspace_bytes, pa_step_graph** graph) {
+  if (!graph) return fail(PA_E_NULL, "graph is required");
+  *graph = nullptr;
+  // Every check the three calls make is made here first, so a bad argument never opens a capture.
+  pa_status st = check_attention_sizes(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads,
+                                       head_dim, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 1 || num_tokens < 1 || num_blocks < 1)
+    return fail(PA_E_SHAPE, "a step graph needs num_seqs, num_tokens and num_blocks >= 1");
+  if (!std::isfinite(scale)) return fail(PA_E_SHAPE, "scale must be finite");
+  if (!q || !k || !v || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !context_lens ||
+      !out || !slot_mapping)
+    return fail(PA_E_NULL, "q, k, v, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, "
+                           "out and slot_mapping are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(out))
+    return fail(PA_E_ALIGN, "q, k, v, k_cache, v_cache and out must be 16-byte aligned");
+  if (dtype == PA_BF16) {
+    const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
+    const size_t need = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype, P).total;
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(PA_E_ALIGN, "workspace must be 16-byte aligned");
+  }
+
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "creating the capture stream");
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return hip_fail(e, "beginning the capture");
+  }
+  g_capturing = true;
+  st = pa_build_slot_mapping(block_tables, query_start_loc, context_lens, num_seqs, max_blocks_per_seq, num_tokens,
+                             positions, slot_mapping, cs);
+  if (st == PA_OK)
+    st = pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
+                              dtype, cs);
+  if (st == PA_OK)
+    st = pa_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out,
+                      num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                      dtype, workspace, workspace_bytes, cs);
+  g_capturing = false;
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (st != PA_OK || e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return st != PA_OK ? st : hip_fail(e, "ending the capture");
+  }
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e, "instantiating the step graph");
+  }
+  *graph = new pa_step_graph{g, x};
+  return PA_OK;
+}
+
+pa_status pa_step_graph_launch(const pa_step_graph* graph, void* stream) {
+  if (!graph) return fail(PA_E_NULL, "graph is required");
+  const hipError_t e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "step graph launch");
+  return PA_OK;
+}
+
+pa_status pa_step_graph_destroy(pa_step_graph* graph) {
+  if (!graph) return PA_OK;
+  hipError_t e = hipGraphExecDestroy(graph->exec);
+  const hipError_t e2 = hipGraphDestroy(graph->graph);
+  delete graph;
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) return hip_fail(e, "destroying the step graph");
   return PA_OK;
 }
 

@@ -8,6 +8,7 @@ path: if libpa.so is missing, or a tensor is not on a GPU, the call raises.
 from __future__ import annotations
 
 import ctypes
+import sys
 
 import torch
 
@@ -180,6 +181,78 @@ def step(q, k, v, k_cache, v_cache, block_tables, seq_lens, query_start_loc, con
     reshape_and_cache(k, v, k_cache, v_cache, slot_mapping)
     return attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out=out,
                      workspace=workspace)
+
+
+class StepGraph:
+    """One step (slot mapping, cache write, attention) recorded as a HIP graph over fixed
+    buffers and replayed with one launch (pa_step_graph_create in pa.h).
+
+    Refill the input tensors in place between replays; the graph keeps their addresses
+    and sizes. ``out``, ``slot_mapping`` ([T] int64), ``workspace`` and ``positions``
+    ([T] int32, optional) are written by every replay. The tensors are kept alive for the
+    graph's lifetime.
+    """
+
+    def __init__(self, q, k, v, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out,
+                 slot_mapping, workspace, positions=None):
+        lib = _lib.load()
+        dev = q.device
+        _need(q, "q", ndim=3)
+        dt = _payload_dtype(q, "q")
+        for t, name in ((k, "k"), (v, "v"), (out, "out")):
+            _need(t, name, q.dtype, 3, dev)
+        _need(k_cache, "k_cache", q.dtype, 4, dev)
+        _need(v_cache, "v_cache", q.dtype, 4, dev)
+        _need(block_tables, "block_tables", torch.int32, 2, dev)
+        for t, name in ((seq_lens, "seq_lens"), (query_start_loc, "query_start_loc"), (context_lens, "context_lens")):
+            _need(t, name, torch.int32, 1, dev)
+        _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+        if positions is not None:
+            _need(positions, "positions", torch.int32, 1, dev)
+        T, hq, d = q.shape
+        nb, hkv = k_cache.shape[0], k_cache.shape[1]
+        S, MB = block_tables.shape
+        if k.shape != (T, hkv, d) or v.shape != k.shape or out.shape != q.shape:
+            raise ValueError("k, v must be [T, Hkv, D] and out [T, Hq, D]")
+        if tuple(k_cache.shape) != (nb, hkv, _lib.BLOCK_SIZE, d) or tuple(v_cache.shape) != (nb, hkv, d, _lib.BLOCK_SIZE):
+            raise ValueError("caches must be [NB, Hkv, 16, D] (keys) and [NB, Hkv, D, 16] (values)")
+        if seq_lens.shape[0] != S or context_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+            raise ValueError("seq_lens/context_lens must be [S] and query_start_loc [S+1]")
+        if slot_mapping.shape[0] < T or (positions is not None and positions.shape[0] < T):
+            raise ValueError("slot_mapping and positions need at least T entries")
+        self._keep = (q, k, v, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, out,
+                      slot_mapping, workspace, positions)
+        self._device = dev
+        self._lib = lib
+        handle = ctypes.c_void_p(0)
+        _check(lib.pa_step_graph_create(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                        _ptr(seq_lens), _ptr(query_start_loc), _ptr(context_lens), float(scale),
+                                        _ptr(out), _ptr(positions), _ptr(slot_mapping), S, MB, T, hq, hkv, d, nb, dt,
+                                        _ptr(workspace), workspace.numel(), ctypes.byref(handle)))
+        self._handle = handle
+
+    def replay(self) -> None:
+        """Launch the recorded step on the current stream."""
+        if not self._handle:
+            raise RuntimeError("StepGraph is closed")
+        stream = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream)
+        _check(self._lib.pa_step_graph_launch(self._handle, stream))
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            _check(self._lib.pa_step_graph_destroy(self._handle))
+            self._handle = None
+            self._keep = None
+
+    def __del__(self):
+        # At interpreter exit the HIP runtime may already be gone: leave the graph to the OS.
+        if sys.is_finalizing():
+            return
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class KernelTimer:

@@ -121,6 +121,30 @@ def test_plan_info_validation(lib):
     assert list(info) == [7, 7, 7, 7]
 
 
+def test_step_graph_validation(lib):
+    """Every rejected creation fails before a capture opens, and leaves the handle NULL."""
+    handle = P(0x1234)
+
+    def create(q=A, k=A, v=A, kc=A, vc=A, bt=A, sl=A, qsl=A, ctx=A, scale=0.125, out=A2, pos=P(0), sm=A, S=4,
+               MB=4, T=4, hq=4, hkv=1, d=64, nb=32, dt=1, ws=A, ws_bytes=1 << 40, graph=True):
+        handle.value = 0x1234
+        return lib.pa_step_graph_create(q, k, v, kc, vc, bt, sl, qsl, ctx, ctypes.c_float(scale), out, pos, sm, S,
+                                        MB, T, hq, hkv, d, nb, dt, ws, ws_bytes,
+                                        ctypes.byref(handle) if graph else None)
+
+    assert create(graph=False) == E_NULL
+    for kw, code in [(dict(dt=4), E_DTYPE), (dict(d=96), E_UNSUP), (dict(hq=6, hkv=4), E_SHAPE),
+                     (dict(T=0), E_SHAPE), (dict(S=0), E_SHAPE), (dict(nb=0), E_SHAPE),
+                     (dict(scale=float("inf")), E_SHAPE), (dict(sm=P(0)), E_NULL), (dict(k=P(0)), E_NULL),
+                     (dict(ctx=P(0)), E_NULL), (dict(v=MIS), E_ALIGN), (dict(out=MIS), E_ALIGN),
+                     (dict(ws=P(0)), E_WS), (dict(ws_bytes=64), E_WS), (dict(ws=MIS), E_ALIGN)]:
+        assert create(**kw) == code, kw
+        assert not handle.value, kw  # NULL on error
+    assert create(dt=0, ws=P(0), ws_bytes=0, sm=P(0)) == E_NULL  # fp32 needs no workspace, still a slot mapping
+    assert lib.pa_step_graph_launch(None, P(0)) == E_NULL
+    assert lib.pa_step_graph_destroy(None) == OK
+
+
 def test_reshape_and_cache_validation(lib):
     def call(k=A, v=A, kc=A, vc=A, sm=A, T=4, hkv=2, d=128, nb=8, dt=1):
         return lib.pa_reshape_and_cache(k, v, kc, vc, sm, T, hkv, d, nb, dt, P(0))

@@ -1,0 +1,134 @@
+"""A whole step (slot mapping, cache write, attention) recorded once as a HIP graph and
+replayed: every replay must equal the eager calls on the same inputs bit for bit, and the
+oracle within the stated tolerance.
+
+The graph is captured over padded buffers (T_pad rows). Each replay refills them in place
+with a different seeded step of the same sequence count: decode rows, a 4-row
+verification sequence and a prefill chunk whose length changes from replay to replay, so
+the padding rows change too. Between replays the program does unrelated eager GPU work
+and synchronises.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workload
+from gpu_support import assert_attention_close, gpu_step, log, oracle_step, require_gpu, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+CTX_HI = 300
+BASE_QLEN = [1, 1, 1, 1, 1, 4, 37, 1]
+S = len(BASE_QLEN)
+T_PAD = sum(BASE_QLEN) + 3
+MB = (CTX_HI + max(BASE_QLEN) + 15) // 16 + 1
+NB = S * MB + 8
+# replay -> (seed, prefill chunk length); the last replay repeats the one before it
+REPLAYS = [(100, 37), (101, 30), (102, 12), (102, 12)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _make(seed, chunk, dtype, hq, hkv, d):
+    rng = np.random.default_rng(seed)
+    qlen = list(BASE_QLEN)
+    qlen[6] = chunk
+    ctx = rng.integers(0, CTX_HI, size=S, endpoint=True)
+    return workload.build_step(ctx, qlen, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                               num_blocks=NB, max_blocks_per_seq=MB, seed=seed, device=DEV,
+                               name=f"graph_{seed}_{chunk}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 16, 4, 128), ("f32", 8, 2, 64), ("bf16", 8, 1, 64)])
+def test_step_graph_replays_match_eager(dtype, hq, hkv, d):
+    import paged_kv_cache_460_amd as pa
+
+    first = _make(*REPLAYS[0], dtype, hq, hkv, d)
+    tdt = first.q.dtype
+    q = torch.zeros(T_PAD, hq, d, dtype=tdt, device=DEV)
+    k = torch.zeros(T_PAD, hkv, d, dtype=tdt, device=DEV)
+    v = torch.zeros(T_PAD, hkv, d, dtype=tdt, device=DEV)
+    kc, vc = torch.empty_like(first.k_cache), torch.empty_like(first.v_cache)
+    bt = torch.empty_like(first.block_tables)
+    seq_lens, ctx = torch.empty_like(first.seq_lens), torch.empty_like(first.context_lens)
+    qsl = torch.empty_like(first.query_start_loc)
+    out = torch.empty(T_PAD, hq, d, dtype=tdt, device=DEV)
+    slots = torch.empty(T_PAD, dtype=torch.int64, device=DEV)
+    pos = torch.empty(T_PAD, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(1, pa.attention_workspace_size(S, MB, T_PAD, hq, hkv, d, tdt)), dtype=torch.uint8,
+                     device=DEV)
+    graph = pa.StepGraph(q, k, v, kc, vc, bt, seq_lens, qsl, ctx, first.scale, out, slots, ws, positions=pos)
+    try:
+        for r, (seed, chunk) in enumerate(REPLAYS):
+            st = _make(seed, chunk, dtype, hq, hkv, d)
+            T = st.num_tokens
+            log(f"[graph] {dtype} hq={hq} hkv={hkv} d={d} replay {r}: seed {seed}, T={T} of {T_PAD}")
+            assert st.block_tables.shape == bt.shape and st.k_cache.shape == kc.shape and st.scale == first.scale
+            for dst, src in ((q, st.q), (k, st.k), (v, st.v)):
+                dst.zero_()
+                dst[:T].copy_(src)
+            for dst, src in ((kc, st.k_cache), (vc, st.v_cache), (bt, st.block_tables), (seq_lens, st.seq_lens),
+                             (ctx, st.context_lens), (qsl, st.query_start_loc)):
+                dst.copy_(src)
+            out.fill_(7.0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+
+            eager = gpu_step(st)
+            assert torch.equal(pos[:T], eager["positions"]), f"replay {r}: positions"
+            assert torch.equal(slots[:T], eager["slots"]), f"replay {r}: slot mapping"
+            assert (slots[T:] == -1).all(), f"replay {r}: padding rows must get slot -1"
+            assert torch.equal(_bits(kc), _bits(eager["k_cache"])), f"replay {r}: key cache"
+            assert torch.equal(_bits(vc), _bits(eager["v_cache"])), f"replay {r}: value cache"
+            assert torch.equal(_bits(out[:T]), _bits(eager["out"])), f"replay {r}: attention output vs eager"
+            assert (out[T:] == 7.0).all(), f"replay {r}: padding rows of out were written"
+            arrays = workload.host_arrays(st)
+            ref = oracle_step(arrays)
+            assert_attention_close(to_f64(out[:T]), ref["out"], arrays["query_start_loc"], dtype,
+                                   label=f"graph replay {r}")
+
+            # unrelated eager work between replays
+            x = torch.randn(1 << 20, device=DEV)
+            assert torch.isfinite((x * 2.0).sum()).item()
+            torch.cuda.synchronize()
+    finally:
+        graph.close()
+
+
+def test_step_graph_replay_is_repeatable_back_to_back():
+    """Several replays queued without host synchronisation give the same bits as one."""
+    import paged_kv_cache_460_amd as pa
+
+    st = workload.make_config("mixed_step_bf16", small=True, device=DEV, seed=4)
+    T = st.num_tokens
+    kc, vc = st.k_cache.clone(), st.v_cache.clone()
+    out = torch.empty_like(st.q)
+    slots = torch.empty(T, dtype=torch.int64, device=DEV)
+    ws = torch.empty(max(1, pa.attention_workspace_size(st.num_seqs, st.max_blocks_per_seq, T, st.num_q_heads,
+                                                        st.num_kv_heads, st.head_dim, st.q.dtype)),
+                     dtype=torch.uint8, device=DEV)
+    graph = pa.StepGraph(st.q, st.k, st.v, kc, vc, st.block_tables, st.seq_lens, st.query_start_loc,
+                         st.context_lens, st.scale, out, slots, ws)
+    try:
+        eager = gpu_step(st)
+        for n in (1, 5):
+            out.zero_()
+            for _ in range(n):
+                graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(out), _bits(eager["out"])), f"{n} replays"
+            assert torch.equal(_bits(kc), _bits(eager["k_cache"]))
+    finally:
+        graph.close()
