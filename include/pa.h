@@ -82,7 +82,10 @@ typedef enum pa_status {
   PA_E_UNSUPPORTED = 4, /* valid but not provided: head_dim not 64/128, G not in 1..16 */
   PA_E_ALIGN = 5,       /* a payload pointer is not 16-byte aligned                    */
   PA_E_WORKSPACE = 6,   /* workspace NULL or smaller than pa_attention_workspace_size  */
-  PA_E_HIP = 7          /* the HIP runtime reported an error (launch or event)        */
+  PA_E_HIP = 7,         /* the HIP runtime reported an error (launch or event)        */
+  PA_E_NO_SPACE = 8,    /* block manager: not enough free KV blocks (nothing changed)  */
+  PA_E_REQUEST = 9      /* block manager: unknown or duplicate request id, or a call
+                           that does not fit the request's state                       */
 } pa_status;
 
 typedef enum pa_dtype {

@@ -1,10 +1,12 @@
-"""CPU oracle for one paged-attention step -- TEST INFRASTRUCTURE, not product code.
+"""CPU oracle for one paged-attention step, and a model of the host-side KV block
+manager (``block_manager``) -- TEST INFRASTRUCTURE, not product code.
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library
 (``paged_kv_cache_460_amd``) and imports nothing from it.
 """
 
+from . import block_manager
 from .paged_attention import (
     BLOCK_SIZE,
     OracleInputError,
@@ -18,6 +20,7 @@ from .paged_attention import (
 
 __all__ = [
     "BLOCK_SIZE",
+    "block_manager",
     "OracleInputError",
     "attention",
     "gather_sequence",

@@ -5,6 +5,7 @@ The computation lives in ``libpa.so`` (C ABI in ``include/pa.h``, HIP kernels in
 """
 
 from ._lib import BLOCK_SIZE, LibraryMissing, LIB_PATH, load as load_library
+from .blocks import BlockManager, NoSpace, block_hash
 from .ops import (
     KernelTimer,
     PAError,
@@ -19,6 +20,9 @@ from .ops import (
 
 __all__ = [
     "BLOCK_SIZE",
+    "BlockManager",
+    "NoSpace",
+    "block_hash",
     "KernelTimer",
     "LIB_PATH",
     "LibraryMissing",

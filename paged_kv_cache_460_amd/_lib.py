@@ -1,4 +1,4 @@
-"""ctypes view of libpa.so (declarations mirror include/pa.h)."""
+"""ctypes view of libpa.so (declarations mirror include/pa.h and include/pa_blocks.h)."""
 
 from __future__ import annotations
 
@@ -20,6 +20,8 @@ STATUS_NAMES = {
     5: "PA_E_ALIGN",
     6: "PA_E_WORKSPACE",
     7: "PA_E_HIP",
+    8: "PA_E_NO_SPACE",
+    9: "PA_E_REQUEST",
 }
 
 KERNEL_KINDS = {
@@ -54,6 +56,19 @@ _SIGNATURES = {
                                             ctypes.POINTER(_P)]),
     "pa_step_graph_launch": (ctypes.c_int, [_P, _P]),
     "pa_step_graph_destroy": (ctypes.c_int, [_P]),
+    "pa_bm_create": (ctypes.c_int, [_I32, _I32, ctypes.c_int, ctypes.POINTER(_P)]),
+    "pa_bm_destroy": (ctypes.c_int, [_P]),
+    "pa_bm_add_request": (ctypes.c_int, [_P, _I64, _P, _I64, ctypes.POINTER(_I64)]),
+    "pa_bm_append_tokens": (ctypes.c_int, [_P, _I64, _P, _I64]),
+    "pa_bm_allocate_slots": (ctypes.c_int, [_P, _I64, _I64]),
+    "pa_bm_free_request": (ctypes.c_int, [_P, _I64]),
+    "pa_bm_build_step": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _I64]),
+    "pa_bm_num_free_blocks": (ctypes.c_int, [_P, ctypes.POINTER(_I32)]),
+    "pa_bm_num_cached_blocks": (ctypes.c_int, [_P, ctypes.POINTER(_I32)]),
+    "pa_bm_request_blocks": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
+    "pa_bm_request_info": (ctypes.c_int, [_P, _I64, _P]),
+    "pa_bm_block_state": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "pa_block_hash_compute": (ctypes.c_int, [ctypes.c_int, _P, _P, _P]),
     "pa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "pa_timing_reset": (ctypes.c_int, []),
     "pa_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 SOURCES = [
     "pa_api.cpp",
+    "block_manager.cpp",
     "slots.hip",
     "scatter.hip",
     "plan.hip",

@@ -95,6 +95,11 @@ hipError_t timed(int kind, hipStream_t stream, F&& fn) {
 
 namespace pa {
 
+pa_status report(pa_status s, const char* detail) {
+  g_last_error = detail;
+  return s;
+}
+
 int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads) {
   if (const char* env = std::getenv("PA_KV_PARTITION")) {
     const long v = std::strtol(env, nullptr, 10);
@@ -152,6 +157,8 @@ const char* pa_status_string(pa_status s) {
     case PA_E_ALIGN: return "PA_E_ALIGN: payload pointer not 16-byte aligned";
     case PA_E_WORKSPACE: return "PA_E_WORKSPACE: workspace missing or too small";
     case PA_E_HIP: return "PA_E_HIP: HIP runtime error";
+    case PA_E_NO_SPACE: return "PA_E_NO_SPACE: not enough free KV blocks";
+    case PA_E_REQUEST: return "PA_E_REQUEST: unknown or duplicate request, or a call out of order";
   }
   return "unknown pa_status";
 }

@@ -92,6 +92,9 @@ hipError_t launch_scatter(const void* k, const void* v, void* k_cache, void* v_c
                           const int64_t* slots, int64_t num_tokens, int32_t num_kv_heads,
                           int32_t head_dim, int32_t elem_bytes, hipStream_t stream);
 hipError_t launch_plan(const AttnParams& p, hipStream_t stream);
+
+// Set this host thread's pa_last_error() detail and return s (for entry points in other files).
+pa_status report(pa_status s, const char* detail);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_reduce(const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);

@@ -15,7 +15,8 @@ import torch
 import paged_kv_cache_460_amd as pa
 from paged_kv_cache_460_amd import _lib
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h")]
 
 P = ctypes.c_void_p
 A = P(0x10000)  # aligned, never dereferenced
@@ -33,9 +34,11 @@ def lib():
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_bound_functions():
@@ -52,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.pa_version() == 1
-    for code in range(8):
+    for code in range(10):
         s = lib.pa_status_string(code).decode()
         assert s.startswith(_lib.STATUS_NAMES[code])
     assert lib.pa_status_string(99).decode().startswith("unknown")
