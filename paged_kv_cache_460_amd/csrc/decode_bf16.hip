@@ -13,8 +13,10 @@
 //    token-major key rows, 16 contiguous bytes per lane) and O^T = V^T P^T, where the
 //    QK accumulator already holds P^T in the B-operand layout, and the dim-major value
 //    block gives each lane 2 x 8 contiguous bytes of V^T (4 keys of block 0, 4 of block 1);
-//  * two blocks (32 keys) per step, with the next step's loads in flight while the
-//    current one computes;
+//  * two blocks (32 keys) per step from two operand buffers in turn: the next step's
+//    loads are in flight while the current one computes. Every step issues the same
+//    loads (past the range the second block repeats the first, masked), which keeps the
+//    compiler's wait counts exact: a step waits only for loads issued a step earlier;
 //  * online softmax in the log2 domain (scale * log2 e folded once), max/sum over the
 //    four lane groups by cross-lane shuffles;
 //  * masked keys are removed by select (-inf score, zeroed value), never by multiplying,
@@ -45,33 +47,27 @@ __device__ inline u32x2 stream_load_u32x2(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
+// Both blocks of a step; past the range the second block repeats the first (valid memory,
+// masked), so every step issues the same loads and the compiler's wait counts stay exact.
 template <int D>
 __device__ inline void load_step(DecodeStep<D>& s, const uint16_t* __restrict__ kc,
                                  const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
                                  int kb, int kend, int hkv, int g, int c, int qd) {
   const int b0 = kb >> 4;
-  const bool has1 = kb + kBlock < kend;
   const int64_t p0 = bt[b0];
+  const int64_t p1 = kb + kBlock < kend ? (int64_t)bt[b0 + 1] : p0;
   const uint16_t* kr0 = kc + ((p0 * hkv + g) * kBlock + c) * D + qd * 8;
   const uint16_t* vr0 = vc + ((p0 * hkv + g) * D + c) * kBlock + qd * 4;
+  const uint16_t* kr1 = kc + ((p1 * hkv + g) * kBlock + c) * D + qd * 8;
+  const uint16_t* vr1 = vc + ((p1 * hkv + g) * D + c) * kBlock + qd * 4;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) s.k0[kk] = *reinterpret_cast<const bf16x8*>(kr0 + kk * 32);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) s.v0[dt] = stream_load_u32x2(vr0 + dt * 16 * kBlock);
-  if (has1) {
-    const int64_t p1 = bt[b0 + 1];
-    const uint16_t* kr1 = kc + ((p1 * hkv + g) * kBlock + c) * D + qd * 8;
-    const uint16_t* vr1 = vc + ((p1 * hkv + g) * D + c) * kBlock + qd * 4;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) s.k1[kk] = *reinterpret_cast<const bf16x8*>(kr1 + kk * 32);
+  for (int kk = 0; kk < D / 32; ++kk) s.k1[kk] = *reinterpret_cast<const bf16x8*>(kr1 + kk * 32);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) s.v1[dt] = stream_load_u32x2(vr1 + dt * 16 * kBlock);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) s.k1[kk] = bf16x8{};
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) s.v1[dt] = u32x2{0u, 0u};
-  }
+  for (int dt = 0; dt < D / 16; ++dt) s.v1[dt] = stream_load_u32x2(vr1 + dt * 16 * kBlock);
 }
 
 }  // namespace
@@ -138,13 +134,8 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
   float lsum = 0.f;
   const float sl2 = p.scale * kLog2e;
 
-  DecodeStep<D> cur;
-  load_step<D>(cur, kc, vc, bt, kbeg, kend, hkv, g, c, qd);
-  for (int kb = kbeg; kb < kend; kb += 2 * kBlock) {
-    DecodeStep<D> nxt;
-    const bool more = kb + 2 * kBlock < kend;
-    if (more) load_step<D>(nxt, kc, vc, bt, kb + 2 * kBlock, kend, hkv, g, c, qd);
-
+  // One step: the 32 keys from kb, operands in cur; updates m, lsum and acc.
+  auto step = [&](const DecodeStep<D>& cur, int kb) {
     // S^T for the two blocks: lane holds keys 4qd..4qd+3 of each block, column c.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -203,7 +194,30 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
       acc[dt] *= alpha;
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pb, acc[dt], 0, 0, 0);
     }
-    if (more) cur = nxt;
+  };
+
+  // Two operand buffers in turn, each step the same loads: the next step's loads go out
+  // before the current step computes, and the current step waits only for loads issued
+  // one step earlier.
+  DecodeStep<D> sa, sb;
+  load_step<D>(sa, kc, vc, bt, kbeg, kend, hkv, g, c, qd);
+  for (int kb = kbeg;;) {
+    if (kb + 2 * kBlock < kend) {
+      load_step<D>(sb, kc, vc, bt, kb + 2 * kBlock, kend, hkv, g, c, qd);
+      step(sa, kb);
+    } else {
+      step(sa, kb);
+      break;
+    }
+    kb += 2 * kBlock;
+    if (kb + 2 * kBlock < kend) {
+      load_step<D>(sa, kc, vc, bt, kb + 2 * kBlock, kend, hkv, g, c, qd);
+      step(sb, kb);
+    } else {
+      step(sb, kb);
+      break;
+    }
+    kb += 2 * kBlock;
   }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
