@@ -53,8 +53,18 @@
  * Errors: arguments are validated on the host before anything is enqueued; a non-OK
  * status means nothing was enqueued, and pa_last_error() gives the detail (per host
  * thread). Index values stored in device memory (block ids, slots, lengths) are not
- * checked: breaking the preconditions below is undefined behaviour. No C++ exception
- * crosses this interface.
+ * checked on the fast path: breaking the preconditions below is undefined behaviour.
+ * No C++ exception crosses this interface.
+ *
+ * Debug mode: with the environment variable PA_DEBUG=1, pa_build_slot_mapping,
+ * pa_reshape_and_cache and pa_attention first run a check kernel over the index arrays
+ * on the call's stream, wait for it (the call synchronises the stream) and return
+ * PA_E_INDEX, with the first violating sequence or token in pa_last_error(), before
+ * enqueuing any work. Checked: query_start_loc[0] = 0, non-decreasing, and
+ * query_start_loc[S] <= T; context_lens >= 0; seq_lens = context_lens + query rows; the
+ * blocks a sequence reads fit in max_blocks_per_seq and their ids lie in [0, NB); slots
+ * lie in [-1, 16 NB) and non-negative slots are distinct (a check quadratic in T). The
+ * mode cannot run inside a stream capture (PA_E_UNSUPPORTED).
  *
  * Preconditions: non-negative slots are pairwise distinct; seq_lens[i] =
  * context_lens[i] + (qsl[i+1] - qsl[i]); every block id a sequence reads lies in
@@ -84,8 +94,9 @@ typedef enum pa_status {
   PA_E_WORKSPACE = 6,   /* workspace NULL or smaller than pa_attention_workspace_size  */
   PA_E_HIP = 7,         /* the HIP runtime reported an error (launch or event)        */
   PA_E_NO_SPACE = 8,    /* block manager: not enough free KV blocks (nothing changed)  */
-  PA_E_REQUEST = 9      /* block manager: unknown or duplicate request id, or a call
+  PA_E_REQUEST = 9,     /* block manager: unknown or duplicate request id, or a call
                            that does not fit the request's state                       */
+  PA_E_INDEX = 10       /* PA_DEBUG=1: an index value breaks a precondition             */
 } pa_status;
 
 typedef enum pa_dtype {

@@ -22,6 +22,7 @@ STATUS_NAMES = {
     7: "PA_E_HIP",
     8: "PA_E_NO_SPACE",
     9: "PA_E_REQUEST",
+    10: "PA_E_INDEX",
 }
 
 KERNEL_KINDS = {

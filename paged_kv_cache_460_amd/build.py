@@ -32,6 +32,7 @@ SOURCES = [
     "reduce.hip",
     "prefill_bf16.hip",
     "attn_f32.hip",
+    "debug_checks.hip",
 ]
 
 ARCH = "gfx950"

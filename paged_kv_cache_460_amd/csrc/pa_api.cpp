@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -33,6 +34,45 @@ pa_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// ---- PA_DEBUG index checks ------------------------------------------------------
+
+bool debug_enabled() {
+  const char* e = std::getenv("PA_DEBUG");
+  return e && e[0] == '1';
+}
+
+const char* check_text(int code) {
+  switch (code) {
+    case pa::kCheckQslStart: return "query_start_loc[0] is not 0";
+    case pa::kCheckQslOrder: return "query_start_loc decreases";
+    case pa::kCheckQslEnd: return "query_start_loc[S] exceeds num_tokens";
+    case pa::kCheckContext: return "context_lens is negative";
+    case pa::kCheckSeqLen: return "seq_lens differs from context_lens + query rows";
+    case pa::kCheckTableWidth: return "the sequence needs more than max_blocks_per_seq blocks";
+    case pa::kCheckBlockId: return "a block id lies outside [0, num_blocks)";
+    case pa::kCheckSlotRange: return "the slot lies outside [-1, 16 * num_blocks)";
+    case pa::kCheckSlotDuplicate: return "the slot repeats an earlier token's slot";
+  }
+  return "unknown violation";
+}
+
+// Runs `check` (a pa::check_* call filling index and code) when PA_DEBUG=1; returns PA_OK
+// if the mode is off or nothing is violated.
+template <class F>
+pa_status debug_check(hipStream_t stream, const char* what, F&& check) {
+  if (!debug_enabled()) return PA_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+    return fail(PA_E_UNSUPPORTED, "PA_DEBUG index checks cannot run inside a stream capture");
+  int64_t index = -1;
+  int code = 0;
+  const hipError_t e = check(&index, &code);
+  if (e != hipSuccess) return hip_fail(e, "PA_DEBUG index check");
+  if (code == 0) return PA_OK;
+  return fail(PA_E_INDEX, "PA_DEBUG (%s): %s %lld: %s", what,
+              code >= pa::kCheckSlotRange ? "token" : "sequence", (long long)index, check_text(code));
+}
 
 int elem_bytes(pa_dtype dt) { return dt == PA_BF16 ? 2 : 4; }
 
@@ -159,6 +199,7 @@ const char* pa_status_string(pa_status s) {
     case PA_E_HIP: return "PA_E_HIP: HIP runtime error";
     case PA_E_NO_SPACE: return "PA_E_NO_SPACE: not enough free KV blocks";
     case PA_E_REQUEST: return "PA_E_REQUEST: unknown or duplicate request, or a call out of order";
+    case PA_E_INDEX: return "PA_E_INDEX: an index value breaks a precondition (PA_DEBUG)";
   }
   return "unknown pa_status";
 }
@@ -178,6 +219,12 @@ pa_status pa_build_slot_mapping(const int32_t* block_tables, const int32_t* quer
   if (!slot_mapping || !query_start_loc) return fail(PA_E_NULL, "slot_mapping and query_start_loc are required");
   if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PA_E_NULL, "block_tables and context_lens are required");
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  // (the block count is not an argument here: only negative block ids are caught)
+  const pa_status dc = debug_check(s, "slot mapping", [&](int64_t* index, int* code) {
+    return pa::check_step_indices(query_start_loc, context_lens, nullptr, block_tables, num_seqs, max_blocks_per_seq,
+                                  num_tokens, INT64_MAX, s, index, code);
+  });
+  if (dc != PA_OK) return dc;
   const hipError_t e = timed(PA_KERNEL_SLOT_MAPPING, s, [&] {
     return pa::launch_slot_mapping(block_tables, query_start_loc, context_lens, num_seqs, max_blocks_per_seq,
                                    num_tokens, positions, slot_mapping, s);
@@ -202,6 +249,10 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_E_ALIGN, "k, v, k_cache and v_cache must be 16-byte aligned");
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const pa_status dc = debug_check(s, "cache write", [&](int64_t* index, int* code) {
+    return pa::check_slot_indices(slot_mapping, num_tokens, num_blocks, s, index, code);
+  });
+  if (dc != PA_OK) return dc;
   const hipError_t e = timed(PA_KERNEL_SCATTER, s, [&] {
     return pa::launch_scatter(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, eb, s);
   });
@@ -271,6 +322,11 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   p.num_blocks = num_blocks;
   p.scale = scale;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const pa_status dc = debug_check(s, "attention", [&](int64_t* index, int* code) {
+    return pa::check_step_indices(query_start_loc, context_lens, seq_lens, block_tables, num_seqs, max_blocks_per_seq,
+                                  num_tokens, num_blocks, s, index, code);
+  });
+  if (dc != PA_OK) return dc;
 
   if (dtype == PA_F32) {
     const hipError_t e = timed(PA_KERNEL_ATTN_F32, s, [&] { return pa::launch_attn_f32(p, s); });

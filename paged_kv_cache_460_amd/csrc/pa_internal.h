@@ -93,6 +93,25 @@ hipError_t launch_scatter(const void* k, const void* v, void* k_cache, void* v_c
                           int32_t head_dim, int32_t elem_bytes, hipStream_t stream);
 hipError_t launch_plan(const AttnParams& p, hipStream_t stream);
 
+// PA_DEBUG index checks (debug_checks.hip). Each enqueues its checks on `stream`, waits
+// for them and returns the first violation: *code = 0 if none, else one of kCheck*, with
+// the sequence (or token) index in *index. seq_lens == nullptr checks the inputs of the
+// slot mapping instead of those of attention.
+constexpr int kCheckQslStart = 1;       // query_start_loc[0] != 0
+constexpr int kCheckQslOrder = 2;       // query_start_loc decreases at sequence i
+constexpr int kCheckQslEnd = 3;         // query_start_loc[S] > num_tokens
+constexpr int kCheckContext = 4;        // context_lens[i] < 0
+constexpr int kCheckSeqLen = 5;         // seq_lens[i] != context_lens[i] + query rows
+constexpr int kCheckTableWidth = 6;     // sequence i needs more than max_blocks_per_seq blocks
+constexpr int kCheckBlockId = 7;        // a block id sequence i uses lies outside [0, NB)
+constexpr int kCheckSlotRange = 8;      // slot_mapping[t] outside [-1, 16 NB)
+constexpr int kCheckSlotDuplicate = 9;  // slot_mapping[t] repeats an earlier token's slot
+hipError_t check_step_indices(const int32_t* qsl, const int32_t* ctx, const int32_t* seq_lens, const int32_t* bt,
+                              int32_t num_seqs, int32_t max_blocks, int64_t num_tokens, int64_t num_blocks,
+                              hipStream_t stream, int64_t* index, int* code);
+hipError_t check_slot_indices(const int64_t* slots, int64_t num_tokens, int64_t num_blocks, hipStream_t stream,
+                              int64_t* index, int* code);
+
 // Set this host thread's pa_last_error() detail and return s (for entry points in other files).
 pa_status report(pa_status s, const char* detail);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t stream);

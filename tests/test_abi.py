@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.pa_version() == 1
-    for code in range(10):
+    for code in range(11):
         s = lib.pa_status_string(code).decode()
         assert s.startswith(_lib.STATUS_NAMES[code])
     assert lib.pa_status_string(99).decode().startswith("unknown")
