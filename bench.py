@@ -106,11 +106,23 @@ def cpu_baseline(step, frac):
     oracle.attention(a["q"], kc, vc, a["block_tables"], a["seq_lens"], a["query_start_loc"], a["context_lens"],
                      a["scale"], rows=sub_rows)
     secs = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] + [1])
+    blas = ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in pools})) or "unknown"
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": len(rows) / secs,
         "unit": "tokens/s",
         "cores": int(threads),
+        "cpu_model": cpu_model,
+        "blas": blas,
         "kind": "oracle",
         "sample": f"every {stride}th row of the step ({len(rows)} of {T} rows, {len(seqs)} sequences), "
                   f"fp64 numpy; cache write + attention for those rows; {secs:.1f} s",
@@ -191,6 +203,15 @@ def main():
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     value = T / (ms_per_step / 1e3)
     log(f"[bench] {ms_per_step:.3f} ms/step")
+    # The spread of single steps: K more steps, each between two events on the stream.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for k in range(args.steps):
+        headline()
+        marks[k + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
+    step_median, step_min = per_step[len(per_step) // 2], per_step[0]
     if graph is not None:
         graph.close()
 
@@ -261,6 +282,8 @@ def main():
             "prefill_flops_per_launch": work["prefill_flops"],
             "scatter_bytes_per_launch": work["scatter_bytes"],
             "execution": mode,
+            "ms_per_step_median": step_median,
+            "ms_per_step_min": step_min,
             "eager_ms_per_step_with_kernel_events": eager_ms_per_step,
         },
     }
