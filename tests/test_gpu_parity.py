@@ -370,6 +370,27 @@ def test_full_prefix_shared():
     assert info["decode_rows"] == 128 and info["shared_prefix_keys"] == 4096, info
 
 
+def test_full_spec_verify(monkeypatch):
+    """64 sequences x 4 rows on the multi-row decode path, at full size: sampled sequences
+    against the oracle, and the planner cuts every sequence into decode partitions (no
+    single-row decode rows, no shared prefix)."""
+    import paged_kv_cache_460_amd as pa
+
+    P = 256
+    monkeypatch.setenv("PA_KV_PARTITION", str(P))
+    step = workload.make_config("spec_verify_bf16", device=DEV)
+    check_sampled(step, _seq_sample(step.num_seqs, 6, 4), "spec_verify_bf16")
+    ws = torch.empty(pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, step.num_tokens,
+                                                 step.num_q_heads, step.num_kv_heads, step.head_dim, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    pa.attention(step.q, step.k_cache, step.v_cache, step.block_tables, step.seq_lens, step.query_start_loc,
+                 step.context_lens, step.scale, workspace=ws)
+    info = pa.attention_plan_info(ws, step.q, step.k_cache, step.block_tables)
+    _, _, L = step.lengths()
+    assert info["decode_rows"] == 0 and info["shared_prefix_keys"] == 0, info
+    assert info["decode_tasks"] == int(sum((int(x) + P - 1) // P for x in L)), info
+
+
 def test_full_long_decode():
     step = workload.make_config("long_decode_bf16", device=DEV)
     check_sampled(step, [0, 9], "long_decode_bf16")
