@@ -73,7 +73,8 @@ __device__ inline void load_step(DecodeStep<D>& s, const uint16_t* __restrict__ 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
+// Two waves per SIMD: the register allocator must fit both operand buffers in 256 registers.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(AttnParams p) {
   const int lane = threadIdx.x;
   const int c = lane & 15;   // MFMA column: query head g*G + c
   const int qd = lane >> 4;  // lane group: dims qd*8.. of each 32-dim chunk; keys 4qd.. of each block
@@ -246,8 +247,8 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(AttnParams p) {
 }
 
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.num_seqs * p.max_parts * p.num_kv_heads;
-  if (grid == 0) return hipSuccess;
+  const int64_t grid = p.decode_wgs;  // bound on the planner's (task, kv head) pairs
+  if (grid <= 0) return hipSuccess;
   if (p.head_dim == 128) {
     hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)grid), dim3(64), 0, stream, p);
   } else {

@@ -2,6 +2,7 @@
 // error reporting and optional per-kernel event timing. Declared in include/pa.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdarg>
@@ -140,27 +141,51 @@ pa_status report(pa_status s, const char* detail) {
   return s;
 }
 
-int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads) {
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads) {
+  const int64_t max_len = (int64_t)max_blocks * kBlock;
+  const int64_t len64 = std::max<int64_t>(64, (max_len + 63) / 64 * 64);
+  int64_t P = 0;
   if (const char* env = std::getenv("PA_KV_PARTITION")) {
     const long v = std::strtol(env, nullptr, 10);
-    if (v >= 64 && v <= 65536 && v % 64 == 0) return (int32_t)v;
+    if (v >= 64 && v <= 65536 && v % 64 == 0) P = v;
   }
-  // One wave streams one (sequence, partition, kv head); waves share HBM, so a long
-  // partition is a slow task and the last tasks set the tail. Aim for about eight
-  // partitions over the longest sequence the block table allows, keep >= 8192 tasks
-  // when the sequences are that long, and stay within 256..2048 tokens.
-  const int64_t max_len = (int64_t)max_blocks * kBlock;
-  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  int32_t P = 2048;
-  while (P > 256 && (int64_t)P * 8 > max_len) P /= 2;
-  while (P > 256 && pairs * ((max_len + P - 1) / P) < 8192) P /= 2;
-  return P;
+  if (P == 0) {
+    // A decode task is one (sequence, partition, kv head) streamed by one wave. Every
+    // task pays a start-up latency before it streams, so few long tasks beat many short
+    // ones, as long as there are enough of them to draw the full HBM rate: aim for one
+    // task per decode wave slot (8 per CU) if every sequence had the longest length the
+    // block table allows, and cut no partition shorter than 256 tokens or longer than
+    // that length.
+    const int64_t pairs = std::max<int64_t>(1, (int64_t)num_seqs * num_kv_heads);
+    const int64_t target = (int64_t)device_cus() * 8;
+    P = (pairs * max_len + target - 1) / target;
+    P = (P + 63) / 64 * 64;
+    P = std::min<int64_t>(std::max<int64_t>(P, 256), std::max<int64_t>(256, len64));
+    P = std::min<int64_t>(P, 1 << 24);
+  }
+  Partitioning r;
+  r.part_tokens = (int32_t)P;
+  // The shared prefix is attended by few, wide tasks (all decode rows at once), so it is
+  // cut finer to give the prefix kernel enough of them.
+  r.prefix_part_tokens = (int32_t)std::min<int64_t>(P, 512);
+  // prefix partitions of the prefix length, then suffix partitions of P >= that length:
+  // at most ceil(max_len / prefix partition) + 1 of them
+  r.max_parts = (int32_t)((max_len + r.prefix_part_tokens - 1) / r.prefix_part_tokens + 1);
+  return r;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
-                                 int32_t head_dim, pa_dtype dtype, int32_t part_tokens) {
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                 int32_t max_parts) {
   WorkspaceLayout w{};
   if (dtype != PA_BF16 || num_seqs == 0) return w;  // the fp32 path needs no workspace
   size_t off = 0;
@@ -168,8 +193,6 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t n
   off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
   w.plan_hdr = off;
   off += align256(sizeof(int32_t) * kHdrSize);
-  // one extra slot per sequence: a shared prefix can split a partition in two
-  const int64_t max_parts = ((int64_t)max_blocks * kBlock + part_tokens - 1) / part_tokens + 1;
   w.dec_tasks = off;
   off += align256(sizeof(int32_t) * (size_t)num_seqs * (size_t)max_parts);
   w.dec_seqs = off;
@@ -282,8 +305,8 @@ pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_s
   const pa_status st = check_attention_sizes(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads,
                                              num_kv_heads, head_dim, dtype);
   if (st != PA_OK) return st;
-  const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
-  *bytes = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype, P).total;
+  const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
+  *bytes = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, part.max_parts).total;
   return PA_OK;
 }
 
@@ -334,13 +357,18 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
     return PA_OK;
   }
 
-  p.part_tokens = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
-  p.max_parts = (int32_t)(((int64_t)max_blocks_per_seq * pa::kBlock + p.part_tokens - 1) / p.part_tokens + 1);
-  const int64_t decode_grid = (int64_t)num_seqs * p.max_parts * num_kv_heads;
-  if (decode_grid > INT32_MAX || (int64_t)num_seqs * p.max_parts > INT32_MAX)
-    return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)decode_grid);
-  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype,
-                                                     p.part_tokens);
+  const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
+  p.part_tokens = part.part_tokens;
+  p.prefix_part_tokens = part.prefix_part_tokens;
+  p.max_parts = part.max_parts;
+  // Decode tasks: at most ceil(max_len / P) suffix partitions per sequence; one workgroup
+  // per (task, kv head) pair of that bound.
+  const int64_t max_len = (int64_t)max_blocks_per_seq * pa::kBlock;
+  const int64_t pairs = (int64_t)num_seqs * ((max_len + p.part_tokens - 1) / p.part_tokens) * num_kv_heads;
+  if (pairs > INT32_MAX || (int64_t)num_seqs * p.max_parts > INT32_MAX)
+    return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)pairs);
+  p.decode_wgs = (int32_t)pairs;
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, p.max_parts);
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", w.total, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -375,14 +403,14 @@ pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, 
                                              head_dim, dtype);
   if (st != PA_OK) return st;
   if (dtype != PA_BF16 || num_seqs == 0 || num_tokens == 0) return PA_OK;  // nothing planned
-  const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
-  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype, P);
+  const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, part.max_parts);
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, workspace_bytes);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(s);
   if (e == hipSuccess)
-    e = hipMemcpy(info, static_cast<const char*>(workspace) + w.plan_hdr, sizeof(int32_t) * pa::kHdrSize,
+    e = hipMemcpy(info, static_cast<const char*>(workspace) + w.plan_hdr, sizeof(int32_t) * pa::kHdrInfo,
                   hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "reading the plan");
   return PA_OK;
@@ -419,8 +447,8 @@ pa_status pa_step_graph_create(const void* q, const void* k, const void* v, void
       !aligned16(out))
     return fail(PA_E_ALIGN, "q, k, v, k_cache, v_cache and out must be 16-byte aligned");
   if (dtype == PA_BF16) {
-    const int32_t P = pa::choose_partition(num_seqs, max_blocks_per_seq, num_kv_heads);
-    const size_t need = pa::workspace_layout(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, dtype, P).total;
+    const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
+    const size_t need = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, part.max_parts).total;
     if (!workspace || workspace_bytes < need)
       return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     if (!aligned16(workspace)) return fail(PA_E_ALIGN, "workspace must be 16-byte aligned");

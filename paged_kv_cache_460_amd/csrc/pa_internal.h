@@ -42,9 +42,11 @@ struct AttnParams {
   int64_t num_blocks;
   float scale;
   // split-KV decode
-  int32_t part_tokens;   // partition length P (multiple of 64)
-  int32_t max_parts;     // partial slots per sequence: ceil(MB * 16 / P) + 1 (a shared
-                         // prefix can split one partition in two)
+  int32_t part_tokens;   // decode partition length P (multiple of 64)
+  int32_t prefix_part_tokens;  // shared-prefix partition length (<= P, multiple of 64)
+  int32_t max_parts;     // partial slots per column: ceil(MB * 16 / prefix partition) + 1
+                         // (prefix partitions, then the suffix's; see choose_partitioning)
+  int32_t decode_wgs;    // decode workgroups (one wave each): a bound on (task, kv head) pairs
   float* part_o;         // [S, Hkv, 16, max_parts, D] unnormalised partial outputs
   float* part_ml;        // [S, Hkv, 16, max_parts, 2] running max (log2 domain) and sum
   // work lists written by the planner
@@ -68,6 +70,7 @@ constexpr int kHdrDecSeqs = 1;      // decode sequences in dec_seqs
 constexpr int kHdrPrefixKeys = 2;   // keys of the shared prefix (0: none)
 constexpr int kHdrPrefixParts = 3;  // partitions the shared prefix is cut into
 constexpr int kHdrSize = 4;
+constexpr int kHdrInfo = 4;         // fields reported by pa_attention_plan_info
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WorkspaceLayout {
@@ -80,9 +83,16 @@ struct WorkspaceLayout {
   size_t total;
 };
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
-                                 int32_t head_dim, pa_dtype dtype, int32_t part_tokens);
-int32_t choose_partition(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads);
+// Partition lengths of a step and the partial slots they need; see choose_partitioning.
+struct Partitioning {
+  int32_t part_tokens;         // decode partitions
+  int32_t prefix_part_tokens;  // shared-prefix partitions
+  int32_t max_parts;           // partial slots per (sequence, kv head, column)
+};
+Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads);
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                 int32_t max_parts);
+int device_cus();  // CUs of the current device
 
 // Kernel launchers (defined next to their kernels). Each returns hipGetLastError().
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* qsl, const int32_t* ctx,

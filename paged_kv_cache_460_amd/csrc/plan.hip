@@ -179,7 +179,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
     p.plan_hdr[kHdrDecTasks] = run;
     p.plan_hdr[kHdrDecSeqs] = total_dec;
     p.plan_hdr[kHdrPrefixKeys] = prefix_keys;
-    p.plan_hdr[kHdrPrefixParts] = (prefix_keys + P - 1) / P;
+    p.plan_hdr[kHdrPrefixParts] = (prefix_keys + p.prefix_part_tokens - 1) / p.prefix_part_tokens;
   }
   __syncthreads();
   for (int i = b; i < e; ++i) {

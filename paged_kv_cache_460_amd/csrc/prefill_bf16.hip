@@ -108,8 +108,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int rest = (int)(u / hkv);
     ct = rest % n_ct;
     const int pp = rest / n_ct;
-    kbeg = pp * p.part_tokens;
-    kmax = min(pkeys, kbeg + p.part_tokens);
+    kbeg = pp * p.prefix_part_tokens;
+    kmax = min(pkeys, kbeg + p.prefix_part_tokens);
     L = pkeys;  // keys at or past the shared prefix are masked (they are not shared)
     seq_or_pp = pp;
     bt = p.block_tables + (int64_t)p.dec_seqs[0] * p.max_blocks;
