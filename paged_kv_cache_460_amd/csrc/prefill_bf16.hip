@@ -12,7 +12,8 @@
 // R = NW * NS * (32 / G) rows. The K/V tiles of the kv head are staged once in LDS and
 // shared by every strip of the workgroup.
 //
-// Per key tile of 64 keys (4 blocks, gathered through the block table):
+// Keys are staged 128 at a time (8 blocks, gathered through the block table) and
+// computed in tiles of 64. Per compute tile:
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read from LDS,
 //    B = Q^T held in registers for the whole tile loop;
 //  * the key rows are fed to the MFMA in a fixed permuted order, chosen so that the
@@ -25,13 +26,15 @@
 //  * masked keys (causal, or past the sequence end) are removed by select, and value
 //    entries past the sequence end are zeroed while staging, so NaN in unwritten slots
 //    cannot leak.
-// Tiles go from global memory straight into LDS (global_load_lds, 16 bytes per lane),
-// double-buffered: the loads of tile t+1 are in flight while tile t is multiplied, and
-// one barrier per tile separates the buffers. Each lane picks the global 16 bytes that
-// belong in its LDS slot, so the tiles land XOR-swizzled in 16-byte units and the
-// 16-byte operand reads of a half-wave hit distinct banks. The compiler does not count
-// these loads as LDS writes, so the kernel waits for them explicitly (vmcnt) before the
-// barrier that publishes a tile.
+// Staged tiles go from global memory straight into LDS (global_load_lds, 16 bytes per
+// lane), double-buffered: the loads of stage s+1 are in flight while stage s is
+// multiplied, and one barrier per stage separates the buffers (two 64 KB buffers for
+// D = 128; a 128-key stage halves the barriers of a 64-key one, which measured faster;
+// the shared-prefix mode stages 64 keys).
+// Each lane picks the global 16 bytes that belong in its LDS slot, so the tiles land
+// XOR-swizzled in 16-byte units and the 16-byte operand reads of a half-wave hit
+// distinct banks. The compiler does not count these loads as LDS writes, so the kernel
+// waits for them explicitly (vmcnt) before the barrier that publishes a stage.
 //
 // Workgroups take tasks last-first: last sequence, last rows first, kv head fastest.
 // For chunks listed in ascending-context order that starts the longest tiles first.
@@ -45,7 +48,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest weight let through unscaled
-constexpr int kTK = 64;              // keys per tile
+constexpr int kTK = 64;              // keys per compute tile
 // s_waitcnt immediate for gfx9: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
@@ -75,8 +78,11 @@ template <int D, int NW, int NS, bool kPrefix>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_kernel(AttnParams p) {
   constexpr int CPR = D / 8;                      // 16-byte chunks per key row
   constexpr int NT = NW * 64;
-  static_assert((16 * D / 64) % NW == 0, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * kTK * D];  // keys, then values
+  // Keys per staged LDS tile: two compute tiles for chunks; one in prefix mode, whose
+  // partitions are short (at most 512 keys), so the extra stage depth does not pay.
+  constexpr int kST = kPrefix ? kTK : 2 * kTK;
+  static_assert((2 * kST * D / 8 / 64) % NW == 0, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * kST * D];  // keys, then values
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
@@ -185,19 +191,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int md = 0; md < D / 32; ++md) o[s][md] = f32x16{};
   }
 
-  // ---- staging: key and value tile of keys [kt, kt + 64), global -> LDS directly ----
-  // The tile is 16*D 16-byte slots: key slots [0, 8D) then value slots [8D, 16D). Each
+  // ---- staging: key and value tile of keys [kt, kt + 128), global -> LDS directly ----
+  // The tile is 32*D 16-byte slots: key slots [0, 16D) then value slots [16D, 32D). Each
   // wave instruction fills 64 consecutive slots (lane i -> slot base + i), so each lane
   // fetches the global 16 bytes that belong in its slot under the XOR swizzle. All 64
   // slots of one instruction lie in one block, so the block id is loaded once per wave.
   // Blocks at or past the sequence end are read from the sequence's first block instead
   // (any valid memory): their keys are masked and their values zeroed before use.
-  constexpr int kSlots = 16 * D;
+  constexpr int kKeySlots = kST * D / 8;  // 16-byte slots of the key part
+  constexpr int kSlots = 2 * kKeySlots;
   constexpr int kInstPerWave = kSlots / 64 / NW;
-  // Block ids of a tile: lane l holds the id of the tile's block l (l < 4); loaded one
-  // tile ahead so that the barrier's wait covers them.
+  constexpr int kStBlocks = kST / kBlock;
+  // Block ids of a staged tile: lane l holds the id of the tile's block l (l < 8); loaded
+  // one tile ahead so that the barrier's wait covers them.
   auto load_ids = [&](int kt) {
-    const int b = (kt >> 4) + (lane & 3);
+    const int b = (kt >> 4) + (lane & (kStBlocks - 1));
     return (b * kBlock < L) ? bt[b] : bt[0];
   };
   auto dma = [&](int buf, int ids) {
@@ -206,39 +214,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int gi = wave * kInstPerWave + j;
       const int s = gi * 64 + lane;
       const uint16_t* srcp;
-      if (gi * 64 < 8 * D) {
+      if (gi * 64 < kKeySlots) {
         const int row = s / CPR;
         const int gc = (s % CPR) ^ key_swz<D>(row);
         const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 / CPR) >> 4);
         srcp = kc + ((phys * hkv + g) * kBlock + (row & 15)) * D + gc * 8;
       } else {
-        const int sv = s - 8 * D;
+        const int sv = s - kKeySlots;
         const int dim = (sv >> 1) % D;
         const int gh = (sv & 1) ^ val_swz(dim);
-        const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 - 8 * D) / (2 * D));
+        const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 - kKeySlots) / (2 * D));
         srcp = vc + ((phys * hkv + g) * D + dim) * kBlock + gh * 8;
       }
       lds_dma16(srcp, &lds[buf][gi * 64 * 8]);
     }
   };
-  // Zero the value entries of keys [L, kt + 64) in a staged tile (only the tile that
+  // Zero the value entries of keys [L, kt + kST) in a staged tile (only the tile that
   // holds the sequence end needs it).
   auto zero_tail = [&](int kt, int buf) {
     const int k0 = max(L, kt);
-    const int nk = kt + kTK - k0;
+    const int nk = kt + kST - k0;
     for (int x = tid; x < nk * D; x += NT) {
       const int key = k0 - kt + x / D;
       const int dim = x % D;
       const int bl = key >> 4, o = key & 15;
-      lds[buf][8 * D * 8 + (bl * D + dim) * kBlock + (((o >> 3) ^ val_swz(dim)) * 8) + (o & 7)] = 0;
+      lds[buf][kST * D + (bl * D + dim) * kBlock + (((o >> 3) ^ val_swz(dim)) * 8) + (o & 7)] = 0;
     }
   };
 
-  // ---- S^T = K Q^T for the 64 keys of one staged key tile ----
-  auto qk = [&](int buf, f32x16 (&sc)[NS][2]) {
+  // ---- S^T = K Q^T for the 64 keys of one half of a staged key tile ----
+  auto qk = [&](int buf, int half, f32x16 (&sc)[NS][2]) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) sc[s][0] = sc[s][1] = f32x16{};
-    const int row0 = perm_key(col);
+    const int row0 = half * kTK + perm_key(col);
     const uint16_t* kr0 = &lds[buf][row0 * D];
     const uint16_t* kr1 = &lds[buf][(32 + row0) * D];
     const int sw0 = key_swz<D>(row0), sw1 = key_swz<D>(32 + row0);
@@ -318,15 +326,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
-  // ---- O^T += V^T P^T for one staged value tile ----
-  auto pv = [&](int buf, bf16x8 (&pf)[NS][4]) {
+  // ---- O^T += V^T P^T for one half of a staged value tile ----
+  auto pv = [&](int buf, int half, bf16x8 (&pf)[NS][4]) {
 #pragma unroll
     for (int md = 0; md < D / 32; ++md) {
       const int dim = md * 32 + col;
       const int sw = val_swz(dim);
 #pragma unroll
       for (int ub = 0; ub < 4; ++ub) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds[buf][8 * D * 8 + (ub * D + dim) * kBlock + ((h2 ^ sw) * 8)]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds[buf][kST * D + ((half * 4 + ub) * D + dim) * kBlock + ((h2 ^ sw) * 8)]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) o[s][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s][ub], o[s][md], 0, 0, 0);
       }
@@ -334,9 +342,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
 
   // ---- tile loop ----
-  // The loads of key/value tile t+1 are in flight while tile t is multiplied; the two
-  // LDS buffers alternate and one barrier per tile separates them. Waves whose rows need
-  // no more keys skip the arithmetic but keep staging and meeting the barrier.
+  // The loads of stage s+1 are in flight while the two compute tiles of stage s are
+  // multiplied; the two LDS buffers alternate and one barrier per stage separates them.
+  // Waves whose rows need no more keys skip the arithmetic but keep staging and meeting
+  // the barrier.
   int wkmax = 0;  // keys this wave's strips need
   int wtm = 1 << 30;  // first tile that needs the mask
 #pragma unroll
@@ -348,31 +357,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   dma(0, load_ids(kbeg));
-  int ids_next = kbeg + kTK < kmax ? load_ids(kbeg + kTK) : 0;
+  int ids_next = kbeg + kST < kmax ? load_ids(kbeg + kST) : 0;
   int buf = 0;
-  for (int kt = kbeg; kt < kmax; kt += kTK, buf ^= 1) {
+  for (int kt = kbeg; kt < kmax; kt += kST, buf ^= 1) {
     // The compiler does not count LDS-DMA loads as LDS writes, so the barrier alone
     // would not wait for them: wait for every outstanding vector-memory operation of
     // this wave (this tile's DMA and the next tile's block ids), then publish.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (kt + kTK > L) {
+    if (kt + kST > L) {
       zero_tail(kt, buf);
       __syncthreads();
     }
-    if (kt + kTK < kmax) {  // the other buffer was released by the barrier above
+    if (kt + kST < kmax) {  // the other buffer was released by the barrier above
       dma(buf ^ 1, ids_next);
-      if (kt + 2 * kTK < kmax) ids_next = load_ids(kt + 2 * kTK);
+      if (kt + 2 * kST < kmax) ids_next = load_ids(kt + 2 * kST);
     }
-    if (kt >= wkmax) continue;
-    f32x16 sc[NS][2];
-    bf16x8 pf[NS][4];
-    float mnew[NS], psum[NS];
-    bool any_raise;
-    qk(buf, sc);
-    softmax_weights(kt, kt / kTK >= wtm, sc, pf, mnew, psum, any_raise);
-    softmax_commit(mnew, psum, any_raise);
-    pv(buf, pf);
+#pragma unroll
+    for (int half = 0; half < kST / kTK; ++half) {
+      const int kh = kt + half * kTK;
+      if (kh >= wkmax) break;
+      f32x16 sc[NS][2];
+      bf16x8 pf[NS][4];
+      float mnew[NS], psum[NS];
+      bool any_raise;
+      qk(buf, half, sc);
+      softmax_weights(kh, kh / kTK >= wtm, sc, pf, mnew, psum, any_raise);
+      softmax_commit(mnew, psum, any_raise);
+      pv(buf, half, pf);
+    }
   }
 
   // ---- epilogue ----
