@@ -54,6 +54,14 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ inline bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// max(x[l], x[l ^ 32]) in every lane: v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second, so with x in both, each lane ends up
+// holding its own value in one result and its partner's in the other.
+__device__ inline float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Key row (within a 32-key half tile) that MFMA row m reads; see the header comment.
 __device__ inline int perm_key(int m) {
   return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
@@ -199,8 +207,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Blocks at or past the sequence end are read from the sequence's first block instead
   // (any valid memory): their keys are masked and their values zeroed before use.
   constexpr int kKeySlots = kST * D / 8;  // 16-byte slots of the key part
-  constexpr int kSlots = 2 * kKeySlots;
-  constexpr int kInstPerWave = kSlots / 64 / NW;
   constexpr int kStBlocks = kST / kBlock;
   // Block ids of a staged tile: lane l holds the id of the tile's block l (l < 8); loaded
   // one tile ahead so that the barrier's wait covers them.
@@ -208,25 +214,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int b = (kt >> 4) + (lane & (kStBlocks - 1));
     return (b * kBlock < L) ? bt[b] : bt[0];
   };
+  // Each wave issues kInstK key copies, then as many value copies.
+  constexpr int kInstK = kKeySlots / 64 / NW;
+  static_assert((kKeySlots / 64) % NW == 0, "key tile must split evenly over the waves");
   auto dma = [&](int buf, int ids) {
 #pragma unroll
-    for (int j = 0; j < kInstPerWave; ++j) {
-      const int gi = wave * kInstPerWave + j;
+    for (int j = 0; j < kInstK; ++j) {
+      const int gi = wave * kInstK + j;
       const int s = gi * 64 + lane;
-      const uint16_t* srcp;
-      if (gi * 64 < kKeySlots) {
-        const int row = s / CPR;
-        const int gc = (s % CPR) ^ key_swz<D>(row);
-        const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 / CPR) >> 4);
-        srcp = kc + ((phys * hkv + g) * kBlock + (row & 15)) * D + gc * 8;
-      } else {
-        const int sv = s - kKeySlots;
-        const int dim = (sv >> 1) % D;
-        const int gh = (sv & 1) ^ val_swz(dim);
-        const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 - kKeySlots) / (2 * D));
-        srcp = vc + ((phys * hkv + g) * D + dim) * kBlock + gh * 8;
-      }
-      lds_dma16(srcp, &lds[buf][gi * 64 * 8]);
+      const int row = s / CPR;
+      const int gc = (s % CPR) ^ key_swz<D>(row);
+      const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 / CPR) >> 4);
+      lds_dma16(kc + ((phys * hkv + g) * kBlock + (row & 15)) * D + gc * 8, &lds[buf][gi * 64 * 8]);
+    }
+#pragma unroll
+    for (int j = 0; j < kInstK; ++j) {
+      const int gi = wave * kInstK + j;
+      const int sv = gi * 64 + lane;
+      const int dim = (sv >> 1) % D;
+      const int gh = (sv & 1) ^ val_swz(dim);
+      const int64_t phys = __builtin_amdgcn_readlane(ids, gi * 64 / (2 * D));
+      lds_dma16(vc + ((phys * hkv + g) * D + dim) * kBlock + gh * 8, &lds[buf][kST * D + gi * 64 * 8]);
     }
   };
   // Zero the value entries of keys [L, kt + kST) in a staged tile (only the tile that
@@ -287,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[s][mt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_across_halves(mx);
       const float mxs = mx * sl2;
       const bool raise = mxs > m[s] + kLazyRescale;
       any_raise |= raise;
