@@ -216,6 +216,9 @@ pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, 
  * padding (rows past query_start_loc[num_seqs] get slot -1 and no output). The graph
  * writes positions (if given), slot_mapping, the caches, out and the workspace: the
  * same writes as the three calls, with the same results.
+ * A bf16 step with num_tokens - num_seqs >= 1024 records the prefill kernel on a graph
+ * branch that runs beside the decode and merge kernels (it writes only the chunk rows of
+ * out); the results are the same.
  * The graph belongs to the device that was current at creation; launch it on a stream
  * of that device. Replays that share buffers must not overlap in time. Kernel timing
  * (pa_timing_*) does not see kernels run from a graph.

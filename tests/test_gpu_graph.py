@@ -132,3 +132,74 @@ def test_step_graph_replay_is_repeatable_back_to_back():
             assert torch.equal(_bits(kc), _bits(eager["k_cache"]))
     finally:
         graph.close()
+
+
+def test_step_graph_with_prefill_branch():
+    """A step with more than 1024 rows beyond one per sequence records the prefill kernel
+    on a graph branch beside the decode and merge kernels. Replays with different chunk
+    lengths, and eager GPU work between them, must still equal the eager calls bit for
+    bit and the oracle within tolerance."""
+    import paged_kv_cache_460_amd as pa
+
+    hq, hkv, d = 16, 4, 128
+    n_dec, ctx_hi = 24, 400
+    chunks = [(7, (600, 700)), (8, (650, 560)), (9, (512, 777))]
+    s = n_dec + 2
+    t_pad = n_dec + max(a + b for _, (a, b) in chunks) + 5
+    assert t_pad - s >= 1024
+    mb = (ctx_hi + 800 + 15) // 16 + 1
+    nb = s * mb + 8
+
+    def make(seed, ab):
+        rng = np.random.default_rng(seed)
+        qlen = [1] * n_dec + list(ab)
+        ctx = rng.integers(0, ctx_hi, size=s, endpoint=True)
+        return workload.build_step(ctx, qlen, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype="bf16",
+                                   num_blocks=nb, max_blocks_per_seq=mb, seed=seed, device=DEV,
+                                   name=f"graph_branch_{seed}")
+
+    first = make(*chunks[0])
+    q = torch.zeros(t_pad, hq, d, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(t_pad, hkv, d, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros(t_pad, hkv, d, dtype=torch.bfloat16, device=DEV)
+    kc, vc = torch.empty_like(first.k_cache), torch.empty_like(first.v_cache)
+    bt = torch.empty_like(first.block_tables)
+    seq_lens, ctx = torch.empty_like(first.seq_lens), torch.empty_like(first.context_lens)
+    qsl = torch.empty_like(first.query_start_loc)
+    out = torch.empty(t_pad, hq, d, dtype=torch.bfloat16, device=DEV)
+    slots = torch.empty(t_pad, dtype=torch.int64, device=DEV)
+    ws = torch.empty(pa.attention_workspace_size(s, mb, t_pad, hq, hkv, d, torch.bfloat16), dtype=torch.uint8,
+                     device=DEV)
+    graph = pa.StepGraph(q, k, v, kc, vc, bt, seq_lens, qsl, ctx, first.scale, out, slots, ws)
+    try:
+        for r, (seed, ab) in enumerate(chunks):
+            st = make(seed, ab)
+            T = st.num_tokens
+            log(f"[graph] prefill branch replay {r}: seed {seed}, chunks {ab}, T={T} of {t_pad}")
+            for dst, src in ((q, st.q), (k, st.k), (v, st.v)):
+                dst.zero_()
+                dst[:T].copy_(src)
+            for dst, src in ((kc, st.k_cache), (vc, st.v_cache), (bt, st.block_tables), (seq_lens, st.seq_lens),
+                             (ctx, st.context_lens), (qsl, st.query_start_loc)):
+                dst.copy_(src)
+            out.fill_(7.0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+
+            eager = gpu_step(st)
+            assert torch.equal(slots[:T], eager["slots"]), f"replay {r}: slot mapping"
+            assert torch.equal(_bits(kc), _bits(eager["k_cache"])), f"replay {r}: key cache"
+            assert torch.equal(_bits(vc), _bits(eager["v_cache"])), f"replay {r}: value cache"
+            assert torch.equal(_bits(out[:T]), _bits(eager["out"])), f"replay {r}: attention output vs eager"
+            assert (out[T:] == 7.0).all(), f"replay {r}: padding rows of out were written"
+            arrays = workload.host_arrays(st)
+            ref = oracle_step(arrays)
+            assert_attention_close(to_f64(out[:T]), ref["out"], arrays["query_start_loc"], "bf16",
+                                   label=f"prefill-branch replay {r}")
+
+            x = torch.randn(1 << 20, device=DEV)
+            assert torch.isfinite((x * 2.0).sum()).item()
+            torch.cuda.synchronize()
+    finally:
+        graph.close()
