@@ -147,7 +147,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "bench.py measures one GPU: --gpus must be 1 (the path does not shard across GPUs)"}), flush=True)
         sys.exit(2)
 
     import torch

@@ -233,7 +233,7 @@ const char* pa_status_string(pa_status s) {
     case PA_E_NULL: return "PA_E_NULL: required pointer is NULL";
     case PA_E_DTYPE: return "PA_E_DTYPE: unknown dtype";
     case PA_E_SHAPE: return "PA_E_SHAPE: invalid or inconsistent size";
-    case PA_E_UNSUPPORTED: return "PA_E_UNSUPPORTED: shape not provided by this build";
+    case PA_E_UNSUPPORTED: return "PA_E_UNSUPPORTED: shape not supported by the library";
     case PA_E_ALIGN: return "PA_E_ALIGN: payload pointer not 16-byte aligned";
     case PA_E_WORKSPACE: return "PA_E_WORKSPACE: workspace missing or too small";
     case PA_E_HIP: return "PA_E_HIP: HIP runtime error";
