@@ -26,15 +26,20 @@
 //  * masked keys (causal, or past the sequence end) are removed by select, and value
 //    entries past the sequence end are zeroed while staging, so NaN in unwritten slots
 //    cannot leak.
-// Staged tiles go from global memory straight into LDS (global_load_lds, 16 bytes per
-// lane), double-buffered: the loads of stage s+1 are in flight while stage s is
-// multiplied, and one barrier per stage separates the buffers (two 64 KB buffers for
-// D = 128; a 128-key stage halves the barriers of a 64-key one, which measured faster;
-// the shared-prefix mode stages 64 keys).
+// Staged tiles go from global memory straight into LDS (buffer loads with an LDS
+// destination, 16 bytes per lane), double-buffered: the loads of stage s+1 are in flight
+// while stage s is multiplied, and one barrier per stage separates the buffers (two
+// 64 KB buffers for D = 128; a 128-key stage halves the barriers of a 64-key one, which
+// measured faster; the shared-prefix mode stages 64 keys).
 // Each lane picks the global 16 bytes that belong in its LDS slot, so the tiles land
 // XOR-swizzled in 16-byte units and the 16-byte operand reads of a half-wave hit
 // distinct banks. The compiler does not count these loads as LDS writes, so the kernel
 // waits for them explicitly (vmcnt) before the barrier that publishes a stage.
+// Buffer loads rather than global_load_lds: the compiler treats the latter as a flat
+// access that may touch LDS, and while one is outstanding (all stage long, by design)
+// it drains every LDS read before its first use (lgkmcnt(0)). With buffer loads the
+// operand reads of a product are waited for one by one, a few slices ahead of the MFMAs
+// that use them.
 //
 // Workgroups take tasks last-first: last sequence, last rows first, kv head fastest.
 // For chunks listed in ascending-context order that starts the longest tiles first.
@@ -67,10 +72,14 @@ __device__ inline int perm_key(int m) {
   return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
 }
 
-// One 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i). Kept out of
-// the kernel template: the builtin only exists for the device compilation.
-__device__ __attribute__((always_inline)) inline void lds_dma16(const uint16_t* src, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+// One 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i), as a buffer
+// load whose resource is one (block, kv head) tile: base is that tile's address (uniform),
+// voff the lane's byte offset inside it.
+__device__ __attribute__((always_inline)) inline void lds_dma16(const void* tile, int tile_bytes, int voff,
+                                                                uint16_t* lds_base) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(tile), (short)0, tile_bytes,
+                                                                     0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
 }
 
 // 16-byte-unit swizzles of the LDS tiles.
@@ -225,7 +234,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int row = s / CPR;
       const int gc = (s % CPR) ^ key_swz<D>(row);
       const int64_t phys = __builtin_amdgcn_readlane(ids, (gi * 64 / CPR) >> 4);
-      lds_dma16(kc + ((phys * hkv + g) * kBlock + (row & 15)) * D + gc * 8, &lds[buf][gi * 64 * 8]);
+      lds_dma16(kc + (phys * hkv + g) * kBlock * D, kBlock * D * 2, ((row & 15) * D + gc * 8) * 2,
+                &lds[buf][gi * 64 * 8]);
     }
 #pragma unroll
     for (int j = 0; j < kInstK; ++j) {
@@ -234,7 +244,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int dim = (sv >> 1) % D;
       const int gh = (sv & 1) ^ val_swz(dim);
       const int64_t phys = __builtin_amdgcn_readlane(ids, gi * 64 / (2 * D));
-      lds_dma16(vc + ((phys * hkv + g) * D + dim) * kBlock + gh * 8, &lds[buf][kST * D + gi * 64 * 8]);
+      lds_dma16(vc + (phys * hkv + g) * D * kBlock, kBlock * D * 2, (dim * kBlock + gh * 8) * 2,
+                &lds[buf][kST * D + gi * 64 * 8]);
     }
   };
   // Zero the value entries of keys [L, kt + kST) in a staged tile (only the tile that
@@ -258,14 +269,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const uint16_t* kr0 = &lds[buf][row0 * D];
     const uint16_t* kr1 = &lds[buf][(32 + row0) * D];
     const int sw0 = key_swz<D>(row0), sw1 = key_swz<D>(32 + row0);
+    bf16x8 a0[D / 16], a1[D / 16];
 #pragma unroll
     for (int kq = 0; kq < D / 16; ++kq) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr0 + (((kq * 2 + h2) ^ sw0) * 8));
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr1 + (((kq * 2 + h2) ^ sw1) * 8));
+      a0[kq] = *reinterpret_cast<const bf16x8*>(kr0 + (((kq * 2 + h2) ^ sw0) * 8));
+      a1[kq] = *reinterpret_cast<const bf16x8*>(kr1 + (((kq * 2 + h2) ^ sw1) * 8));
+    }
+#pragma unroll
+    for (int kq = 0; kq < D / 16; ++kq) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        sc[s][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s][kq], sc[s][0], 0, 0, 0);
-        sc[s][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s][kq], sc[s][1], 0, 0, 0);
+        sc[s][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[kq], qf[s][kq], sc[s][0], 0, 0, 0);
+        sc[s][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[kq], qf[s][kq], sc[s][1], 0, 0, 0);
       }
     }
   };
@@ -335,18 +350,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
 
   // ---- O^T += V^T P^T for one half of a staged value tile ----
-  auto pv = [&](int buf, int half, bf16x8 (&pf)[NS][4]) {
+  auto pv_load = [&](int buf, int half, bf16x8 (&va)[D / 32][4]) {
 #pragma unroll
-    for (int md = 0; md < D / 32; ++md) {
-      const int dim = md * 32 + col;
-      const int sw = val_swz(dim);
+    for (int ub = 0; ub < 4; ++ub) {
 #pragma unroll
-      for (int ub = 0; ub < 4; ++ub) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds[buf][kST * D + ((half * 4 + ub) * D + dim) * kBlock + ((h2 ^ sw) * 8)]);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) o[s][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s][ub], o[s][md], 0, 0, 0);
+      for (int md = 0; md < D / 32; ++md) {
+        const int dim = md * 32 + col;
+        const int sw = val_swz(dim);
+        va[md][ub] = *reinterpret_cast<const bf16x8*>(&lds[buf][kST * D + ((half * 4 + ub) * D + dim) * kBlock + ((h2 ^ sw) * 8)]);
       }
     }
+  };
+  auto pv = [&](const bf16x8 (&va)[D / 32][4], bf16x8 (&pf)[NS][4]) {
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub)
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) o[s][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md][ub], pf[s][ub], o[s][md], 0, 0, 0);
   };
 
   // ---- tile loop ----
@@ -389,10 +410,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       bf16x8 pf[NS][4];
       float mnew[NS], psum[NS];
       bool any_raise;
+      bf16x8 va[D / 32][4];
       qk(buf, half, sc);
+      pv_load(buf, half, va);
+      // Instruction order: the first 3 key slices (6 reads), then each pair of QK MFMAs
+      // followed by the reads 3 slices ahead; the value reads fill in behind the last
+      // MFMAs and land while the softmax runs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int j = 0; j < D / 16 - 3; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, D / 8 - 8, 0);
       softmax_weights(kh, kh / kTK >= wtm, sc, pf, mnew, psum, any_raise);
       softmax_commit(mnew, psum, any_raise);
-      pv(buf, half, pf);
+      pv(va, pf);
     }
   }
 
