@@ -77,7 +77,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   __shared__ int32_t bcount[kBuckets];
   __shared__ int32_t bfill[kBuckets];
   __shared__ int32_t boff[kBuckets];
-  __shared__ int32_t mismatch;
   const int32_t* __restrict__ qsl = p.qsl;
   const int32_t* __restrict__ seq_lens = p.seq_lens;
   const int num_seqs = p.num_seqs;
@@ -141,16 +140,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
     const int cap = block_min(sums, tid, cap_local);
     const int all_same_first = block_min(sums, tid, same_first);
     if (all_same_first && cap >= kMinPrefixBlocks) {
-      if (tid == 0) mismatch = cap;
-      __syncthreads();
-      const int64_t pairs = (int64_t)num_seqs * cap;
-      for (int64_t k = tid; k < pairs; k += 1024) {
-        const int i = (int)(k / cap);
-        const int c = (int)(k % cap);
-        if (qsl[i + 1] - qsl[i] == 1 && p.block_tables[(int64_t)i * MB + c] != bref[c]) atomicMin(&mismatch, c);
+      // Wave w compares sequences w, w + 16, ... four at a time, its lanes over the
+      // blocks; each lane keeps the first mismatching block it saw. The comparisons are
+      // selects, not branches, so all loads of a round are in flight together.
+      const int lane = tid & 63, w = tid >> 6;
+      int bad = cap;
+      for (int i0 = w; i0 < num_seqs; i0 += 4 * 16) {
+        bool dec[4];
+        const int32_t* __restrict__ row[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + 16 * u;
+          dec[u] = i < num_seqs && qsl[i + 1] - qsl[i] == 1;
+          row[u] = p.block_tables + (int64_t)min(i, num_seqs - 1) * MB;
+        }
+        for (int c = lane; c < cap; c += 64) {
+          const int r = bref[c];
+          int x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = row[u][c];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) bad = (dec[u] && x[u] != r) ? min(bad, c) : bad;
+        }
       }
-      __syncthreads();
-      prefix_blocks = mismatch;
+      prefix_blocks = block_min(sums, tid, bad);
     }
   }
   if (prefix_blocks < kMinPrefixBlocks) prefix_blocks = 0;
