@@ -175,9 +175,10 @@ def test_shared_prefix_equals_private_copies():
     assert_attention_close(to_f64(a), to_f64(b), qsl, "bf16", label="shared vs private")
 
 
-def _shared_prefix_step(prefix_blocks, suffix_lens, hq, hkv, d, chunks=(), seed=21, unshared=False):
+def _shared_prefix_step(prefix_blocks, suffix_lens, hq, hkv, d, chunks=(), seed=21, unshared=False, diverge=None):
     """Decode sequences that all list the same `prefix_blocks` blocks first (plus optional
-    prefill chunks that do not share them)."""
+    prefill chunks that do not share them). `diverge` = (sequence, block): that sequence
+    shares only the blocks before `block` and keeps its own blocks from there on."""
     ctx = [prefix_blocks * 16 + s - 1 for s in suffix_lens] + [c for c, _ in chunks]
     qlen = [1] * len(suffix_lens) + [n for _, n in chunks]
     step = workload.build_step(ctx, qlen, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype="bf16", seed=seed,
@@ -187,6 +188,9 @@ def _shared_prefix_step(prefix_blocks, suffix_lens, hq, hkv, d, chunks=(), seed=
     shared = bt[0, :prefix_blocks].clone()
     last = S_dec - 1 if unshared else S_dec
     bt[1:last, :prefix_blocks] = shared
+    if diverge is not None:
+        j, k = diverge
+        bt[j, k:prefix_blocks] = step.block_tables[j, k:prefix_blocks]
     step.block_tables = bt
     # the shared blocks must hold the same data the first sequence sees: they are its blocks
     return step
@@ -222,6 +226,13 @@ SHARED_PREFIX_CASES = {
     "g3_d64": (5, [8, 1, 50, 17], 6, 2, 64, (), False),
     "long_prefix_many_parts": (300, [1, 100, 513], 8, 1, 128, (), False),
     "one_sequence_does_not_share": (12, [5, 9, 33, 2], 8, 2, 128, (), True),
+    # one sequence leaves the shared run early: the prefix is the shorter run (at least
+    # 4 blocks) or nothing
+    "diverge_at_block_5": (12, [5, 9, 33, 2], 8, 2, 128, (), False, (2, 5)),
+    "diverge_at_block_3": (12, [5, 9, 33, 2], 8, 2, 128, (), False, (1, 3)),
+    # 150 decode rows (several rounds of the planner's per-wave comparison) and a
+    # divergence past the first 64 blocks, found by a sequence far down the list
+    "many_rows_diverge_past_64": (100, [1 + (7 * i) % 90 for i in range(150)], 8, 2, 64, (), False, (137, 70)),
 }
 
 
@@ -231,8 +242,9 @@ def test_shared_prefix_cases(case):
     and the planner must have found exactly the shared run (or none)."""
     import paged_kv_cache_460_amd as pa
 
-    nb, suf, hq, hkv, d, chunks, unshared = SHARED_PREFIX_CASES[case]
-    step = _shared_prefix_step(nb, suf, hq, hkv, d, chunks=chunks, unshared=unshared)
+    nb, suf, hq, hkv, d, chunks, unshared, *rest = SHARED_PREFIX_CASES[case]
+    diverge = rest[0] if rest else None
+    step = _shared_prefix_step(nb, suf, hq, hkv, d, chunks=chunks, unshared=unshared, diverge=diverge)
     check_full(step, f"shared_prefix/{case}")
     # the same step again with a workspace we keep, to read the plan back
     kc, vc = step.k_cache.clone(), step.v_cache.clone()
@@ -242,7 +254,8 @@ def test_shared_prefix_cases(case):
             step.context_lens, step.scale, workspace=ws)
     info = pa.attention_plan_info(ws, step.q, kc, step.block_tables)
     assert info["decode_rows"] == len(suf)
-    assert info["shared_prefix_keys"] == (0 if unshared else 16 * nb), info
+    shared_blocks = 0 if unshared else (nb if diverge is None else diverge[1])
+    assert info["shared_prefix_keys"] == (16 * shared_blocks if shared_blocks >= 4 else 0), info
 
 
 def test_sequence_order_does_not_matter():
