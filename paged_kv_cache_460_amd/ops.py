@@ -246,8 +246,12 @@ class StepGraph:
             self._keep = None
 
     def __del__(self):
-        # At interpreter exit the HIP runtime may already be gone: leave the graph to the OS.
-        if sys.is_finalizing():
+        # At interpreter exit the HIP runtime may already be gone (and this module's
+        # globals cleared): leave the graph to the OS.
+        try:
+            if sys.is_finalizing():
+                return
+        except Exception:
             return
         try:
             self.close()
