@@ -12,8 +12,8 @@
 // R = NW * NS * (32 / G) rows. The K/V tiles of the kv head are staged once in LDS and
 // shared by every strip of the workgroup.
 //
-// Keys are staged 128 at a time (8 blocks, gathered through the block table) and
-// computed in tiles of 64. Per compute tile:
+// Keys are staged 64 at a time (4 blocks, gathered through the block table; 128 with
+// 8-wave workgroups) and computed in tiles of 64. Per compute tile:
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read from LDS,
 //    B = Q^T held in registers for the whole tile loop;
 //  * the key rows are fed to the MFMA in a fixed permuted order, chosen so that the
@@ -29,8 +29,7 @@
 // Staged tiles go from global memory straight into LDS (buffer loads with an LDS
 // destination, 16 bytes per lane), double-buffered: the loads of stage s+1 are in flight
 // while stage s is multiplied, and one barrier per stage separates the buffers (two
-// 64 KB buffers for D = 128; a 128-key stage halves the barriers of a 64-key one, which
-// measured faster; the shared-prefix mode stages 64 keys).
+// 32 KB buffers for D = 128).
 // Each lane picks the global 16 bytes that belong in its LDS slot, so the tiles land
 // XOR-swizzled in 16-byte units and the 16-byte operand reads of a half-wave hit
 // distinct banks. The compiler does not count these loads as LDS writes, so the kernel
@@ -95,9 +94,9 @@ template <int D, int NW, int NS, bool kPrefix>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_kernel(AttnParams p) {
   constexpr int CPR = D / 8;                      // 16-byte chunks per key row
   constexpr int NT = NW * 64;
-  // Keys per staged LDS tile: two compute tiles for chunks; one in prefix mode, whose
-  // partitions are short (at most 512 keys), so the extra stage depth does not pay.
-  constexpr int kST = kPrefix ? kTK : 2 * kTK;
+  // Keys per staged LDS tile: one compute tile, so that two workgroups fit a CU's LDS
+  // (with 8-wave workgroups, one per CU, chunks stage two compute tiles per barrier).
+  constexpr int kST = (kPrefix || NW < 8) ? kTK : 2 * kTK;
   static_assert((2 * kST * D / 8 / 64) % NW == 0, "tile must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * kST * D];  // keys, then values
 
@@ -208,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int md = 0; md < D / 32; ++md) o[s][md] = f32x16{};
   }
 
-  // ---- staging: key and value tile of keys [kt, kt + 128), global -> LDS directly ----
+  // ---- staging: key and value tile of keys [kt, kt + kST), global -> LDS directly ----
   // The tile is 32*D 16-byte slots: key slots [0, 16D) then value slots [16D, 32D). Each
   // wave instruction fills 64 consecutive slots (lane i -> slot base + i), so each lane
   // fetches the global 16 bytes that belong in its slot under the XOR swizzle. All 64
@@ -471,8 +470,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-// Workgroup shape: waves per workgroup and 32-column strips per wave.
-constexpr int kPrefillWaves = 8;
+// Workgroup shape: waves per workgroup and 32-column strips per wave. Two 4-wave
+// workgroups share a CU (one wave of each per SIMD, 64 KB of LDS each); each meets only
+// its own barriers, so the two waves of a SIMD drift out of step and one's MFMA work
+// overlaps the other's softmax. One 8-wave workgroup per CU keeps them in lockstep:
+// 2.5% slower, although it stages each key/value tile for twice the rows.
+constexpr int kPrefillWaves = 4;
 constexpr int kPrefillStrips = 1;
 
 int prefill_rows_per_tile(int group) { return kPrefillWaves * kPrefillStrips * (32 / group); }
