@@ -5,8 +5,9 @@
 // row reads every cached K/V byte of its sequence once, so this kernel is built to
 // stream whole 16-token blocks from HBM at full rate:
 //
-//  * one wave = one (sequence, kv partition of P tokens, kv head), taken in the
-//    planner's longest-first order. All G query heads of the kv head ride in the N
+//  * one wave = one (sequence, kv partition, kv head), taken in the planner's
+//    longest-first order; a sequence's range is cut into ceil(len / P) partitions of
+//    about equal length (split_parts). All G query heads of the kv head ride in the N
 //    dimension of one 16x16x32 MFMA, so each K/V byte is read once for the whole GQA
 //    group (columns past G are zero and ignored);
 //  * transposed products: S^T = K Q^T (A = 16 keys x 32 dims straight from the block's
@@ -101,9 +102,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const bool multi = nrows > 1;
   const int prefix_keys = multi ? 0 : p.plan_hdr[kHdrPrefixKeys];
   const int prefix_parts = multi ? 0 : p.plan_hdr[kHdrPrefixParts];
-  const int kbeg = prefix_keys + part * P;
-  const int kend = min(L, kbeg + P);
-  const int nparts = prefix_parts + (L - prefix_keys + P - 1) / P;
+  const PartSplit sp = split_parts(L - prefix_keys, P);
+  const int kbeg = prefix_keys + part * sp.plen;
+  const int kend = min(L, kbeg + sp.plen);
+  const int nparts = prefix_parts + sp.n;
   const int slot_part = prefix_parts + part;
   // column c = (row r, head-in-group hh); row r sits at position L - nrows + r and sees
   // keys up to it (causal), so its keys stop at climit

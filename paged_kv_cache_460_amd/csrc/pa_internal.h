@@ -64,6 +64,22 @@ __host__ __device__ inline int64_t part_slot(const AttnParams& p, int i, int q, 
   return (((int64_t)i * p.num_kv_heads + g) * 16 + c) * p.max_parts + q;
 }
 
+// Decode-path KV partitions of a range of `len` keys: n partitions of plen keys, the last
+// one shorter. plen is len / ceil(len / P) rounded up to whole 32-key steps (never above
+// P), so a sequence's partitions are about equally long instead of full P-key ones and a
+// short remainder; n <= ceil(len / P), and every partition holds at least one key.
+struct PartSplit {
+  int n;
+  int plen;
+};
+__host__ __device__ inline PartSplit split_parts(int len, int P) {
+  if (len <= 0) return {0, P};
+  const int n0 = (len + P - 1) / P;
+  int plen = ((len + n0 - 1) / n0 + 31) / 32 * 32;
+  plen = plen < P ? plen : P;
+  return {(len + plen - 1) / plen, plen};
+}
+
 // plan_hdr fields
 constexpr int kHdrDecTasks = 0;     // decode tasks in dec_tasks
 constexpr int kHdrDecSeqs = 1;      // decode sequences in dec_seqs

@@ -16,12 +16,13 @@
 //  * sequences of 2..16/G rows (speculative verification) take the decode path as well:
 //    their (row, head) pairs fill the MFMA columns and their whole KV range is cut
 //    into partitions like a decode suffix;
-//  * each decode suffix is cut into KV partitions of P tokens. dec_tasks lists every
-//    (sequence, partition) longest first: all full partitions, then the partial last
-//    partitions in 32 length buckets, longest bucket first. Workgroups are dispatched in
-//    list order, so the last ones to start are the shortest and the tail of the decode
-//    launch is short. (The order inside a bucket depends on timing; each task's result
-//    does not.)
+//  * each decode suffix is cut into ceil(len / P) KV partitions of about equal length
+//    (split_parts: whole 32-key steps, at most P). dec_tasks lists every (sequence,
+//    partition) longest first: those of exactly P keys in sequence order, then the others
+//    in 32 length buckets, longest bucket first. Workgroups are dispatched in list
+//    order, so the last ones to start are the shortest and the tail of the decode launch
+//    is short. (The order inside a bucket depends on timing; each task's result does
+//    not.)
 //
 // One workgroup of 1024 threads: each thread takes a contiguous run of sequences,
 // counts, and after block-wide scans and reductions writes its entries.
@@ -175,11 +176,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
     const int n = qsl[i + 1] - qsl[i];
     return n == 1 ? seq_lens[i] - prefix_keys : (is_multi(n) ? seq_lens[i] : 0);
   };
+  // Tasks of exactly P keys come first, in sequence order; the others follow in 32 length
+  // buckets, longest bucket first.
+  auto bucket = [&](int tlen) { return (tlen - 1) * kBuckets / P; };
+  auto tlen_of = [&](const PartSplit& sp, int len, int q) { return q + 1 < sp.n ? sp.plen : len - (sp.n - 1) * sp.plen; };
   int full = 0;
   for (int i = b; i < e; ++i) {
     const int len = task_len(i);
-    full += len / P;
-    if (len % P) atomicAdd(&bcount[(len % P - 1) * kBuckets / P], 1);
+    const PartSplit sp = split_parts(len, P);
+    for (int q = 0; q < sp.n; ++q) {
+      const int t = tlen_of(sp, len, q);
+      if (t == P) ++full;
+      else atomicAdd(&bcount[bucket(t)], 1);
+    }
   }
   int total_full;
   int full_run = block_exclusive_scan(sums, tid, full, total_full);
@@ -197,12 +206,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   __syncthreads();
   for (int i = b; i < e; ++i) {
     const int len = task_len(i);
-    const int nfull = len / P;
-    for (int q = 0; q < nfull; ++q) p.dec_tasks[full_run + q] = i * p.max_parts + q;
-    full_run += nfull;
-    if (len % P) {
-      const int k = (len % P - 1) * kBuckets / P;
-      p.dec_tasks[boff[k] + atomicAdd(&bfill[k], 1)] = i * p.max_parts + nfull;
+    const PartSplit sp = split_parts(len, P);
+    for (int q = 0; q < sp.n; ++q) {
+      const int t = tlen_of(sp, len, q);
+      const int slot = t == P ? full_run++ : boff[bucket(t)] + atomicAdd(&bfill[bucket(t)], 1);
+      p.dec_tasks[slot] = i * p.max_parts + q;
     }
   }
 }

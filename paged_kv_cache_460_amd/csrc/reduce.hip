@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnParams p) {
   const int P = p.part_tokens;
   const int prefix_keys = nrows == 1 ? p.plan_hdr[kHdrPrefixKeys] : 0;
   const int prefix_parts = nrows == 1 ? p.plan_hdr[kHdrPrefixParts] : 0;
-  const int nparts = prefix_parts + (p.seq_lens[i] - prefix_keys + P - 1) / P;
+  const int nparts = prefix_parts + split_parts(p.seq_lens[i] - prefix_keys, P).n;
   if (nparts <= 1) return;  // the decode kernel wrote the rows itself
   const int cs = lane / kLpc;  // column within the pass
   const int j = lane % kLpc;   // partition stride (max pass), 4-dim group (sum pass)

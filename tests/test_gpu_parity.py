@@ -383,6 +383,14 @@ def test_full_prefix_shared():
     assert info["decode_rows"] == 128 and info["shared_prefix_keys"] == 4096, info
 
 
+def _decode_partitions(length, P):
+    """Partitions of a decode-path KV range: ceil(length / P) of about equal length, each a
+    whole number of 32-key steps and at most P, so possibly one fewer."""
+    n0 = -(-length // P)
+    plen = min(P, -(-(-(-length // n0)) // 32) * 32)
+    return -(-length // plen)
+
+
 def test_full_spec_verify(monkeypatch):
     """64 sequences x 4 rows on the multi-row decode path, at full size: sampled sequences
     against the oracle, and the planner cuts every sequence into decode partitions (no
@@ -401,7 +409,7 @@ def test_full_spec_verify(monkeypatch):
     info = pa.attention_plan_info(ws, step.q, step.k_cache, step.block_tables)
     _, _, L = step.lengths()
     assert info["decode_rows"] == 0 and info["shared_prefix_keys"] == 0, info
-    assert info["decode_tasks"] == int(sum((int(x) + P - 1) // P for x in L)), info
+    assert info["decode_tasks"] == int(sum(_decode_partitions(int(x), P) for x in L)), info
 
 
 def test_full_long_decode():
