@@ -73,7 +73,10 @@ __device__ inline int perm_key(int m) {
 
 // One 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i), as a buffer
 // load whose resource is one (block, kv head) tile: base is that tile's address (uniform),
-// voff the lane's byte offset inside it.
+// voff the lane's byte offset inside it. The resource's last word (0x00020000) selects a
+// 32-bit data format, the usual setting for raw (untyped) buffer loads on this family;
+// with stride 0 and num_records = the tile's bytes, an offset past the tile would read
+// zeros instead of memory outside it (the offsets here all lie inside).
 __device__ __attribute__((always_inline)) inline void lds_dma16(const void* tile, int tile_bytes, int voff,
                                                                 uint16_t* lds_base) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(tile), (short)0, tile_bytes,
