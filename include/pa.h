@@ -171,7 +171,9 @@ pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_s
  * to rounding (requests sharing cached prefix blocks: shengyayun.com blog, 关键实现细节
  * item 2).
  * Environment: PA_KV_PARTITION=<tokens> (a multiple of 64 in [64, 65536]) overrides
- * the split-KV partition length that decode rows use.
+ * the split-KV partition length P that decode rows use: a decode-path range of len keys
+ * is cut into ceil(len / P) partitions of about equal length (whole 32-key steps, at
+ * most P keys each).
  * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED, PA_E_ALIGN,
  * PA_E_WORKSPACE, PA_E_HIP.
  */
