@@ -217,7 +217,10 @@ pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, 
  * so a caller refills them in place between replays; a step with fewer rows fits by
  * padding (rows past query_start_loc[num_seqs] get slot -1 and no output). The graph
  * writes positions (if given), slot_mapping, the caches, out and the workspace: the
- * same writes as the three calls, with the same results.
+ * same writes as the three calls, with the same results. The slot mapping, the cache
+ * write and the planner run as one launch in the graph (they are independent of each
+ * other, and everything after them needs all three), so a replay crosses two fewer kernel
+ * boundaries than the three calls.
  * A bf16 step with num_tokens - num_seqs >= 1024 records the prefill kernel on a graph
  * branch that runs beside the decode and merge kernels (it writes only the chunk rows of
  * out); the results are the same.

@@ -124,6 +124,16 @@ struct PrefillBranch {
 };
 thread_local const PrefillBranch* g_prefill_branch = nullptr;
 
+// Set while pa_step_graph_create records a step: the slot-mapping and cache-write calls
+// check their arguments and leave them here instead of launching, and the attention call
+// makes one launch for both and the planner (pa::launch_step_prologue), which saves two
+// kernel boundaries per replay.
+struct StepPrologue {
+  pa::PrologueArgs a{};
+  bool slots = false, cache = false, launched = false;
+};
+thread_local StepPrologue* g_prologue = nullptr;
+
 // Rows beyond one per sequence from which a step graph runs prefill on a branch. Measured
 // on one MI355X, replays of the two graphs alternated in one process: with 3 x 2048 chunk
 // rows beside 1664 decode rows the step took 5.092 ms with the branch and 5.136 ms
@@ -265,6 +275,19 @@ pa_status pa_build_slot_mapping(const int32_t* block_tables, const int32_t* quer
                                   num_tokens, INT64_MAX, s, index, code);
   });
   if (dc != PA_OK) return dc;
+  if (g_prologue) {
+    pa::PrologueArgs& a = g_prologue->a;
+    a.block_tables = block_tables;
+    a.qsl = query_start_loc;
+    a.ctx = context_lens;
+    a.num_seqs = num_seqs;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_tokens = num_tokens;
+    a.positions = positions;
+    a.slots = slot_mapping;
+    g_prologue->slots = true;
+    return PA_OK;
+  }
   const hipError_t e = timed(PA_KERNEL_SLOT_MAPPING, s, [&] {
     return pa::launch_slot_mapping(block_tables, query_start_loc, context_lens, num_seqs, max_blocks_per_seq,
                                    num_tokens, positions, slot_mapping, s);
@@ -293,6 +316,20 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
     return pa::check_slot_indices(slot_mapping, num_tokens, num_blocks, s, index, code);
   });
   if (dc != PA_OK) return dc;
+  if (g_prologue) {
+    pa::PrologueArgs& a = g_prologue->a;
+    if (!g_prologue->slots || a.slots != slot_mapping || a.num_tokens != num_tokens)
+      return fail(PA_E_SHAPE, "a recorded step writes the caches with the slot mapping it builds");
+    a.k = k;
+    a.v = v;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.elem_bytes = eb;
+    g_prologue->cache = true;
+    return PA_OK;
+  }
   const hipError_t e = timed(PA_KERNEL_SCATTER, s, [&] {
     return pa::launch_scatter(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, eb, s);
   });
@@ -368,7 +405,16 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   });
   if (dc != PA_OK) return dc;
 
+  // In a recorded step the slot mapping and cache write run here, in the planner's launch
+  // (none for fp32).
+  StepPrologue* const pro = g_prologue && g_prologue->cache ? g_prologue : nullptr;
+  if (pro) pro->launched = true;
+
   if (dtype == PA_F32) {
+    if (pro) {
+      const hipError_t e = pa::launch_step_prologue(pro->a, nullptr, s);
+      if (e != hipSuccess) return hip_fail(e, "step prologue launch");
+    }
     const hipError_t e = timed(PA_KERNEL_ATTN_F32, s, [&] { return pa::launch_attn_f32(p, s); });
     if (e != hipSuccess) return hip_fail(e, "fp32 attention launch");
     return PA_OK;
@@ -399,7 +445,9 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   p.part_ml = reinterpret_cast<float*>(base + w.part_ml);
 
   const PrefillBranch* br = g_capturing ? g_prefill_branch : nullptr;
-  hipError_t e = timed(PA_KERNEL_PLAN, s, [&] { return pa::launch_plan(p, s); });
+  hipError_t e = timed(PA_KERNEL_PLAN, s, [&] {
+    return pro ? pa::launch_step_prologue(pro->a, &p, s) : pa::launch_plan(p, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   if (br) {
     e = hipEventRecord(br->planned, s);
@@ -507,8 +555,10 @@ pa_status pa_step_graph_create(const void* q, const void* k, const void* v, void
     release();
     return hip_fail(e, "beginning the capture");
   }
+  StepPrologue prologue;
   g_capturing = true;
   g_prefill_branch = branch ? &br : nullptr;
+  g_prologue = &prologue;
   st = pa_build_slot_mapping(block_tables, query_start_loc, context_lens, num_seqs, max_blocks_per_seq, num_tokens,
                              positions, slot_mapping, cs);
   if (st == PA_OK)
@@ -520,6 +570,9 @@ pa_status pa_step_graph_create(const void* q, const void* k, const void* v, void
                       dtype, workspace, workspace_bytes, cs);
   g_capturing = false;
   g_prefill_branch = nullptr;
+  g_prologue = nullptr;
+  if (st == PA_OK && !prologue.launched)
+    st = fail(PA_E_SHAPE, "the step's slot mapping and cache write were not launched");
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(cs, &g);
   release();

@@ -119,6 +119,24 @@ hipError_t launch_scatter(const void* k, const void* v, void* k_cache, void* v_c
                           int32_t head_dim, int32_t elem_bytes, hipStream_t stream);
 hipError_t launch_plan(const AttnParams& p, hipStream_t stream);
 
+// Arguments of the slot mapping and the cache write, for the step prologue: one launch
+// that builds the slots, writes the caches and, when `plan` is given, runs the planner.
+struct PrologueArgs {
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const int32_t* ctx;
+  int32_t num_seqs, max_blocks;
+  int64_t num_tokens;
+  int32_t* positions;  // may be null
+  int64_t* slots;
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+  int32_t num_kv_heads, head_dim, elem_bytes;
+};
+hipError_t launch_step_prologue(const PrologueArgs& a, const AttnParams* plan, hipStream_t stream);
+
 // PA_DEBUG index checks (debug_checks.hip). Each enqueues its checks on `stream`, waits
 // for them and returns the first violation: *code = 0 if none, else one of kCheck*, with
 // the sequence (or token) index in *index. seq_lens == nullptr checks the inputs of the

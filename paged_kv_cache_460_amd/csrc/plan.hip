@@ -25,8 +25,10 @@
 //    not.)
 //
 // One workgroup of 1024 threads: each thread takes a contiguous run of sequences,
-// counts, and after block-wide scans and reductions writes its entries.
-#include "pa_internal.h"
+// counts, and after block-wide scans and reductions writes its entries. A recorded step
+// runs the planner in the same launch as the slot mapping and the cache write (the step
+// prologue at the end of this file).
+#include "cache_write.h"
 
 namespace pa {
 
@@ -73,7 +75,8 @@ __device__ inline int block_min(int32_t* wsum, int tid, int value) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_per_tile) {
+// The planner, run by one workgroup of 1024 threads.
+__device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
   __shared__ int32_t sums[16];  // per-wave partial results of the block reductions
   __shared__ int32_t bcount[kBuckets];
   __shared__ int32_t bfill[kBuckets];
@@ -215,8 +218,70 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_p
   }
 }
 
+__global__ __launch_bounds__(1024) void plan_kernel(AttnParams p, int32_t rows_per_tile) {
+  plan_block(p, rows_per_tile);
+}
+
 hipError_t launch_plan(const AttnParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p, prefill_rows_per_tile(p.group));
+  return hipGetLastError();
+}
+
+// ---- step prologue ----------------------------------------------------------------
+// Slot mapping, cache write and planner of one step in a single launch of 1024-thread
+// workgroups. They are independent of each other (the planner reads only the length
+// arrays and block tables; the cache write needs the slots of its own 16 tokens, which
+// it derives itself), and the attention kernels after them need all three, so one launch
+// replaces three back-to-back ones. Workgroup 0 plans (when a plan is asked for); every
+// other workgroup takes four cache-write units, one per 256 threads, each first writing
+// the positions and slots of its 16 tokens (kv head 0 only) and keeping them in LDS.
+// The results are those of the three separate launches, bit for bit.
+template <int kElemBytes>
+__global__ __launch_bounds__(1024) void step_prologue_kernel(PrologueArgs a, AttnParams p, int32_t rows_per_tile,
+                                                             int32_t plan_wgs) {
+  if ((int)blockIdx.x < plan_wgs) {
+    plan_block(p, rows_per_tile);
+    return;
+  }
+  __shared__ int64_t unit_slots[4][kWriteGroup];
+  const int quarter = threadIdx.x >> 8, lt = threadIdx.x & 255;
+  const int64_t unit = (int64_t)(blockIdx.x - plan_wgs) * 4 + quarter;
+  const int64_t units = (a.num_tokens + kWriteGroup - 1) / kWriteGroup * a.num_kv_heads;
+  const bool live = unit < units;
+  const int h = live ? (int)(unit % a.num_kv_heads) : 0;
+  const int64_t t0 = live ? unit / a.num_kv_heads * kWriteGroup : 0;
+  if (lt < kWriteGroup) {
+    const int64_t t = t0 + lt;
+    int64_t slot = -1;
+    if (live && t < a.num_tokens) {
+      int32_t pos;
+      slot = token_slot(a.block_tables, a.qsl, a.ctx, a.num_seqs, a.max_blocks, t, pos);
+      if (h == 0) {
+        if (a.positions) a.positions[t] = pos;
+        a.slots[t] = slot;
+      }
+    }
+    unit_slots[quarter][lt] = slot;
+  }
+  __syncthreads();
+  if (!live) return;
+  write_unit<kElemBytes>(static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v),
+                         static_cast<uint8_t*>(a.k_cache), static_cast<uint8_t*>(a.v_cache), t0, h, a.num_tokens,
+                         a.num_kv_heads, a.head_dim, lt, 256, [&](int j) { return unit_slots[quarter][j]; });
+}
+
+hipError_t launch_step_prologue(const PrologueArgs& a, const AttnParams* plan, hipStream_t stream) {
+  const int64_t units = (a.num_tokens + kWriteGroup - 1) / kWriteGroup * a.num_kv_heads;
+  const int32_t plan_wgs = plan ? 1 : 0;
+  const int64_t grid = plan_wgs + (units + 3) / 4;
+  if (grid == 0) return hipSuccess;
+  const AttnParams p = plan ? *plan : AttnParams{};
+  const int32_t rows = plan ? prefill_rows_per_tile(plan->group) : 0;
+  if (a.elem_bytes == 2) {
+    hipLaunchKernelGGL(step_prologue_kernel<2>, dim3((unsigned)grid), dim3(1024), 0, stream, a, p, rows, plan_wgs);
+  } else {
+    hipLaunchKernelGGL(step_prologue_kernel<4>, dim3((unsigned)grid), dim3(1024), 0, stream, a, p, rows, plan_wgs);
+  }
   return hipGetLastError();
 }
 

@@ -203,3 +203,61 @@ def test_step_graph_with_prefill_branch():
             torch.cuda.synchronize()
     finally:
         graph.close()
+
+
+# (dtype, hq, hkv, d, query lengths, padding rows): in a recorded step one 1024-thread
+# workgroup takes four cache-write units of (16 tokens, kv head); these shapes leave the
+# last workgroup with one, two or three of them, and a last group of 16 tokens that is cut
+# short
+RAGGED_PROLOGUE = {
+    "five_units_g1": ("bf16", 4, 1, 128, [1, 1, 1, 1, 40, 20], 6),
+    "nine_units_f32": ("f32", 6, 3, 64, [1, 17, 1, 3, 2], 16),
+    "six_units_tail": ("bf16", 8, 2, 64, [1, 1, 30, 1], 0),
+    "eleven_units": ("bf16", 8, 1, 128, [1] * 9 + [150, 5, 1], 7),
+}
+
+
+@pytest.mark.parametrize("case", sorted(RAGGED_PROLOGUE))
+def test_step_graph_ragged_prologue(case):
+    import paged_kv_cache_460_amd as pa
+
+    dtype, hq, hkv, d, qlen, pad = RAGGED_PROLOGUE[case]
+    s = len(qlen)
+    rng = np.random.default_rng(len(case))
+    ctx = rng.integers(0, 90, size=s, endpoint=True)
+    mb = (90 + max(qlen) + 15) // 16 + 1
+    st = workload.build_step(ctx, qlen, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                             num_blocks=s * mb + 3, max_blocks_per_seq=mb, seed=31, device=DEV, name=case)
+    T = st.num_tokens
+    t_pad = T + pad
+    log(f"[graph] ragged prologue {case}: T={T} of {t_pad}, kv heads {hkv}, units {(t_pad + 15) // 16 * hkv}")
+    tdt = st.q.dtype
+    q, k, v = (torch.zeros(t_pad, *x.shape[1:], dtype=tdt, device=DEV) for x in (st.q, st.k, st.v))
+    q[:T].copy_(st.q)
+    k[:T].copy_(st.k)
+    v[:T].copy_(st.v)
+    kc, vc = st.k_cache.clone(), st.v_cache.clone()
+    out = torch.full((t_pad, hq, d), 7.0, dtype=tdt, device=DEV)
+    slots = torch.full((t_pad,), -5, dtype=torch.int64, device=DEV)
+    pos = torch.full((t_pad,), -5, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(1, pa.attention_workspace_size(s, mb, t_pad, hq, hkv, d, tdt)), dtype=torch.uint8,
+                     device=DEV)
+    graph = pa.StepGraph(q, k, v, kc, vc, st.block_tables, st.seq_lens, st.query_start_loc, st.context_lens,
+                         st.scale, out, slots, ws, positions=pos)
+    try:
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = gpu_step(st)
+        assert torch.equal(pos[:T], eager["positions"]), "positions"
+        assert torch.equal(slots[:T], eager["slots"]), "slot mapping"
+        assert (slots[T:] == -1).all() and (pos[T:] == 0).all(), "padding rows get slot -1 and position 0"
+        assert torch.equal(_bits(kc), _bits(eager["k_cache"])), "key cache"
+        assert torch.equal(_bits(vc), _bits(eager["v_cache"])), "value cache"
+        assert torch.equal(_bits(out[:T]), _bits(eager["out"])), "attention output vs eager"
+        assert (out[T:] == 7.0).all(), "padding rows of out were written"
+        arrays = workload.host_arrays(st)
+        ref = oracle_step(arrays)
+        assert np.array_equal(slots[:T].cpu().numpy(), ref["slots"]), "slot mapping vs oracle"
+        assert_attention_close(to_f64(out[:T]), ref["out"], arrays["query_start_loc"], dtype, label=case)
+    finally:
+        graph.close()
