@@ -261,3 +261,57 @@ def test_step_graph_ragged_prologue(case):
         assert_attention_close(to_f64(out[:T]), ref["out"], arrays["query_start_loc"], dtype, label=case)
     finally:
         graph.close()
+
+
+# (prefix blocks, suffix lengths incl. the new token, Hq, Hkv, D, chunks as (ctx, rows)):
+# decode rows sharing leading blocks, beside short chunks (no prefill branch): the graph
+# records the planner's shared-prefix launch, and replays must find the prefix again
+SHARED_PREFIX_GRAPHS = {
+    "g4_with_chunks": (9, [1, 2, 15, 40], 16, 4, 128, ((0, 70), (40, 33))),
+    "g3_d64": (5, [8, 1, 50, 17], 6, 2, 64, ()),
+    "many_parts": (300, [1, 100, 513], 8, 1, 128, ((20, 5),)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SHARED_PREFIX_GRAPHS))
+def test_step_graph_shared_prefix(case):
+    import paged_kv_cache_460_amd as pa
+
+    prefix_blocks, suffix_lens, hq, hkv, d, chunks = SHARED_PREFIX_GRAPHS[case]
+    ctx = [prefix_blocks * 16 + s - 1 for s in suffix_lens] + [c for c, _ in chunks]
+    qlen = [1] * len(suffix_lens) + [n for _, n in chunks]
+    st = workload.build_step(ctx, qlen, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype="bf16", seed=23,
+                             device=DEV, name=case)
+    bt = st.block_tables.clone()
+    bt[1:len(suffix_lens), :prefix_blocks] = bt[0, :prefix_blocks]
+    st.block_tables = bt
+    T, S = st.num_tokens, st.num_seqs
+    assert T - S < 1024  # one stream: no prefill branch
+    kc, vc = st.k_cache.clone(), st.v_cache.clone()
+    out = torch.full_like(st.q, 7.0)
+    slots = torch.empty(T, dtype=torch.int64, device=DEV)
+    ws = torch.empty(pa.attention_workspace_size(S, st.max_blocks_per_seq, T, hq, hkv, d, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    graph = pa.StepGraph(st.q, st.k, st.v, kc, vc, st.block_tables, st.seq_lens, st.query_start_loc,
+                         st.context_lens, st.scale, out, slots, ws)
+    try:
+        eager = gpu_step(st)
+        for r in range(2):
+            log(f"[graph] shared prefix {case} replay {r}: T={T}, S={S}")
+            kc.copy_(st.k_cache)
+            vc.copy_(st.v_cache)
+            out.fill_(7.0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            info = pa.attention_plan_info(ws, st.q, kc, st.block_tables)
+            assert info["shared_prefix_keys"] == 16 * prefix_blocks, info
+            assert torch.equal(slots, eager["slots"]), f"replay {r}: slot mapping"
+            assert torch.equal(_bits(kc), _bits(eager["k_cache"])), f"replay {r}: key cache"
+            assert torch.equal(_bits(vc), _bits(eager["v_cache"])), f"replay {r}: value cache"
+            assert torch.equal(_bits(out), _bits(eager["out"])), f"replay {r}: attention output vs eager"
+        arrays = workload.host_arrays(st)
+        ref = oracle_step(arrays)
+        assert_attention_close(to_f64(out), ref["out"], arrays["query_start_loc"], "bf16", label=case)
+    finally:
+        graph.close()
