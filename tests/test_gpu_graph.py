@@ -264,12 +264,14 @@ def test_step_graph_ragged_prologue(case):
 
 
 # (prefix blocks, suffix lengths incl. the new token, Hq, Hkv, D, chunks as (ctx, rows)):
-# decode rows sharing leading blocks, beside short chunks (no prefill branch): the graph
-# records the planner's shared-prefix launch, and replays must find the prefix again
+# decode rows sharing leading blocks, beside chunks: the graph records the planner's
+# shared-prefix launch, and replays must find the prefix again
 SHARED_PREFIX_GRAPHS = {
     "g4_with_chunks": (9, [1, 2, 15, 40], 16, 4, 128, ((0, 70), (40, 33))),
     "g3_d64": (5, [8, 1, 50, 17], 6, 2, 64, ()),
     "many_parts": (300, [1, 100, 513], 8, 1, 128, ((20, 5),)),
+    # a chunk of 1100 rows: the prefill and shared-prefix launches go on the graph branch
+    "with_prefill_branch": (12, [1, 9, 33, 2, 70], 16, 4, 128, ((30, 1100),)),
 }
 
 
@@ -286,7 +288,7 @@ def test_step_graph_shared_prefix(case):
     bt[1:len(suffix_lens), :prefix_blocks] = bt[0, :prefix_blocks]
     st.block_tables = bt
     T, S = st.num_tokens, st.num_seqs
-    assert T - S < 1024  # one stream: no prefill branch
+    assert (T - S >= 1024) == (case == "with_prefill_branch")
     kc, vc = st.k_cache.clone(), st.v_cache.clone()
     out = torch.full_like(st.q, 7.0)
     slots = torch.empty(T, dtype=torch.int64, device=DEV)
