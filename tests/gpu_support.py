@@ -41,8 +41,10 @@ def gpu_step(step: workload.Step, out_pool: bool = True):
     pos, slots = pa.build_slot_mapping(step.block_tables, step.query_start_loc, step.context_lens,
                                        num_tokens=step.num_tokens)
     pa.reshape_and_cache(step.k, step.v, kc, vc, slots)
-    out = pa.attention(step.q, kc, vc, step.block_tables, step.seq_lens, step.query_start_loc, step.context_lens,
-                       step.scale)
+    # NaN beforehand: a row that no kernel writes fails the comparison
+    out = torch.full_like(step.q, float("nan"))
+    pa.attention(step.q, kc, vc, step.block_tables, step.seq_lens, step.query_start_loc, step.context_lens,
+                 step.scale, out=out)
     torch.cuda.synchronize()
     res = {"positions": pos, "slots": slots, "out": out}
     if out_pool:

@@ -1,0 +1,250 @@
+"""Full-size parity: every output row of every full-size workload against the oracle.
+
+Each workload runs once through libpa (slot mapping, cache write, attention) on copies of
+its pools, with ``out`` filled with NaN beforehand, so a row that no kernel writes fails.
+Then:
+* positions and slots: bit-exact against the oracle's slot mapping, all tokens;
+* the cache write: the whole pool after the write equals the pool before it with each
+  written slot replaced by its token's bits (every slot, written or not, bit for bit);
+  for the smaller pools also against the oracle's own copy of the write;
+* attention: every row, elementwise within abs 1e-2 / rel 2e-2 plus the per-sequence
+  norm bound, with the oracle run on groups of sequences (each group cut out of the
+  pre-write pools, so the oracle sees the same inputs and writes the new tokens itself).
+The GPU result of a workload is kept between the tests that check its groups, and freed
+when the next workload starts.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+from gpu_support import assert_attention_close, log, oracle_step, payload_bits, require_gpu, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+
+
+_CACHE = {}
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def full_run(name, **kw):
+    """The workload's inputs and libpa's results (cached for the module, one at a time)."""
+    key = (name, tuple(sorted(kw.items())))
+    if key in _CACHE:
+        return _CACHE[key]
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+    import paged_kv_cache_460_amd as pa
+
+    step = workload.make_config(name, device=DEV, **kw)
+    log(f"[full] {name}: S={step.num_seqs} T={step.num_tokens} NB={step.num_blocks} "
+        f"Hq={step.num_q_heads} Hkv={step.num_kv_heads} D={step.head_dim}")
+    kc, vc = step.k_cache.clone(), step.v_cache.clone()
+    pos, slots = pa.build_slot_mapping(step.block_tables, step.query_start_loc, step.context_lens,
+                                       num_tokens=step.num_tokens)
+    pa.reshape_and_cache(step.k, step.v, kc, vc, slots)
+    out = torch.full_like(step.q, float("nan"))
+    pa.attention(step.q, kc, vc, step.block_tables, step.seq_lens, step.query_start_loc, step.context_lens,
+                 step.scale, out=out)
+    torch.cuda.synchronize()
+    res = {"step": step, "positions": pos, "slots": slots, "k_cache": kc, "v_cache": vc, "out": out}
+    _CACHE[key] = res
+    return res
+
+
+def check_indices_and_pool(res, label, oracle_pool):
+    """Slots bit-exact; the whole pool after the write, bit for bit."""
+    step = res["step"]
+    bt = step.block_tables.cpu().numpy()
+    qsl = step.query_start_loc.cpu().numpy()
+    ctx = step.context_lens.cpu().numpy()
+    ref_pos, ref_slots = oracle.slot_mapping(bt, qsl, ctx)
+    assert np.array_equal(res["positions"].cpu().numpy(), ref_pos), f"{label}: positions"
+    assert np.array_equal(res["slots"].cpu().numpy(), ref_slots), f"{label}: slot mapping"
+    # expected pools: the pre-write pools with each written slot replaced by its token
+    slots = res["slots"]
+    live = slots >= 0
+    s = slots[live]
+    exp_k = step.k_cache.clone()
+    exp_v = step.v_cache.clone()
+    exp_k[s // 16, :, s % 16, :] = step.k[live]
+    exp_v[s // 16, :, :, s % 16] = step.v[live]
+    assert torch.equal(_bits(res["k_cache"]), _bits(exp_k)), f"{label}: key pool after the write"
+    assert torch.equal(_bits(res["v_cache"]), _bits(exp_v)), f"{label}: value pool after the write"
+    del exp_k, exp_v
+    if oracle_pool:
+        a = workload.host_arrays(step)
+        ek, ev = oracle.reshape_and_cache(a["k"], a["v"], a["k_cache"], a["v_cache"], ref_slots)
+        kb, vb = payload_bits(res["k_cache"]), payload_bits(res["v_cache"])
+        assert np.array_equal(kb, ek.view(kb.dtype)), f"{label}: key pool vs the oracle's write"
+        assert np.array_equal(vb, ev.view(vb.dtype)), f"{label}: value pool vs the oracle's write"
+    log(f"[full] {label}: slots and whole pools bit-exact")
+
+
+def seq_groups(step, kv_budget_tokens, seqs=None):
+    """Consecutive groups of `seqs` (default: all sequences) holding about
+    `kv_budget_tokens` keys each."""
+    _, _, L = step.lengths()
+    seqs = range(step.num_seqs) if seqs is None else seqs
+    groups, cur, acc = [], [], 0
+    for i in seqs:
+        n = int(L[i])
+        if cur and acc + n > kv_budget_tokens:
+            groups.append(cur)
+            cur, acc = [], 0
+        cur.append(int(i))
+        acc += n
+    if cur:
+        groups.append(cur)
+    return groups
+
+
+def check_rows(res, seqs, label):
+    """Every row of `seqs` against the oracle (run on those sequences alone)."""
+    step = res["step"]
+    sub = workload.subset_sequences(step, seqs, compact_pool=True)
+    arrays = workload.host_arrays(sub)
+    ref = oracle_step(arrays)["out"]
+    qsl = step.query_start_loc.cpu().numpy()
+    rows = np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in seqs])
+    got = to_f64(res["out"][torch.from_numpy(rows).to(DEV)])
+    err = assert_attention_close(got, ref, arrays["query_start_loc"], step.dtype, label=label)
+    return err, rows.size
+
+
+def check_all_groups(res, groups, label):
+    worst, nrows = 0.0, 0
+    for k, seqs in enumerate(groups):
+        err, n = check_rows(res, seqs, f"{label} sequences {seqs[0]}..{seqs[-1]}")
+        worst, nrows = max(worst, err), nrows + n
+    log(f"[full] {label}: {nrows} rows in {len(groups)} groups match; max abs err {worst:.3e}")
+    return nrows
+
+
+def rows_of(step):
+    return int(step.query_start_loc[-1].item())
+
+
+# ---------------------------------------------------------------------------------------
+
+def test_full_decode_batch():
+    res = full_run("decode_batch_bf16")
+    step = res["step"]
+    check_indices_and_pool(res, "decode_batch_bf16", oracle_pool=True)
+    n = check_all_groups(res, seq_groups(step, 64 * 1024), "decode_batch_bf16")
+    assert n == rows_of(step) == 64
+
+
+def test_full_prefix_shared():
+    import paged_kv_cache_460_amd as pa
+
+    res = full_run("prefix_shared_bf16")
+    step = res["step"]
+    check_indices_and_pool(res, "prefix_shared_bf16", oracle_pool=True)
+    n = check_all_groups(res, seq_groups(step, 128 * 1024), "prefix_shared_bf16")
+    assert n == rows_of(step) == 128
+    # all 128 decode rows share the 256-block (4096-token) prefix: the planner finds it
+    ws = torch.empty(pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, step.num_tokens,
+                                                 step.num_q_heads, step.num_kv_heads, step.head_dim, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.full_like(step.q, float("nan"))
+    pa.attention(step.q, res["k_cache"], res["v_cache"], step.block_tables, step.seq_lens, step.query_start_loc,
+                 step.context_lens, step.scale, out=out, workspace=ws)
+    info = pa.attention_plan_info(ws, step.q, res["k_cache"], step.block_tables)
+    assert info["decode_rows"] == 128 and info["shared_prefix_keys"] == 4096, info
+    assert torch.equal(_bits(out), _bits(res["out"])), "second call differs from the first"
+
+
+def _decode_partitions(length, P):
+    """Partitions of a decode-path KV range: ceil(length / P) of about equal length, each a
+    whole number of 32-key steps and at most P, so possibly one fewer."""
+    n0 = -(-length // P)
+    plen = min(P, -(-(-(-length // n0)) // 32) * 32)
+    return -(-length // plen)
+
+
+def test_full_spec_verify(monkeypatch):
+    """64 sequences x 4 rows on the multi-row decode path, 256-token partitions: every row
+    against the oracle, and the planner cuts every sequence into decode partitions."""
+    import paged_kv_cache_460_amd as pa
+
+    P = 256
+    monkeypatch.setenv("PA_KV_PARTITION", str(P))
+    _CACHE.clear()
+    res = full_run("spec_verify_bf16")
+    step = res["step"]
+    check_indices_and_pool(res, "spec_verify_bf16", oracle_pool=True)
+    n = check_all_groups(res, seq_groups(step, 64 * 1024), "spec_verify_bf16")
+    assert n == rows_of(step) == 256
+    ws = torch.empty(pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, step.num_tokens,
+                                                 step.num_q_heads, step.num_kv_heads, step.head_dim, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    pa.attention(step.q, res["k_cache"], res["v_cache"], step.block_tables, step.seq_lens, step.query_start_loc,
+                 step.context_lens, step.scale, workspace=ws)
+    info = pa.attention_plan_info(ws, step.q, res["k_cache"], step.block_tables)
+    _, _, L = step.lengths()
+    assert info["decode_rows"] == 0 and info["shared_prefix_keys"] == 0, info
+    assert info["decode_tasks"] == int(sum(_decode_partitions(int(x), P) for x in L)), info
+    _CACHE.clear()  # results depend on the partition length set above
+
+
+# The mixed step: 1664 decode rows and three 2048-row chunks. Its pool (31.5 GB) is too
+# large to copy whole to the host, so the pool is checked on the device and the rows in
+# four parts, each a short test: three thirds of the decode rows, then the chunks.
+MIXED_PARTS = 4
+
+
+def _mixed_parts(step):
+    S = step.num_seqs
+    dec = seq_groups(step, 512 * 1024, seqs=range(S - 3))
+    third = -(-len(dec) // 3)
+    return [dec[:third], dec[third:2 * third], dec[2 * third:], [[S - 3], [S - 2], [S - 1]]]
+
+
+@pytest.mark.parametrize("part", range(MIXED_PARTS))
+def test_full_mixed_step(part):
+    res = full_run("mixed_step_bf16")
+    step = res["step"]
+    if part == 0:
+        check_indices_and_pool(res, "mixed_step_bf16", oracle_pool=False)
+        assert torch.isfinite(res["out"].float()).all(), "mixed_step_bf16: unwritten rows"
+    n = check_all_groups(res, _mixed_parts(step)[part], f"mixed_step_bf16 part {part}")
+    assert n > 0
+
+
+def test_full_mixed_step_rows_covered():
+    """The four parts above compare every sequence of the mixed step exactly once."""
+    res = full_run("mixed_step_bf16")
+    step = res["step"]
+    seen = sorted(i for part in _mixed_parts(step) for g in part for i in g)
+    assert seen == list(range(step.num_seqs))
+
+
+@pytest.mark.parametrize("half", range(2))
+def test_full_long_decode(half):
+    res = full_run("long_decode_bf16")
+    step = res["step"]
+    if half == 0:
+        check_indices_and_pool(res, "long_decode_bf16", oracle_pool=False)
+        assert torch.isfinite(res["out"].float()).all(), "long_decode_bf16: unwritten rows"
+    S = step.num_seqs
+    mine = list(range(S))[half * S // 2:(half + 1) * S // 2]
+    n = check_all_groups(res, [[i] for i in mine], f"long_decode_bf16 half {half}")
+    assert n == len(mine)
+    if half == 1:
+        _CACHE.clear()

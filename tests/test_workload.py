@@ -76,3 +76,16 @@ def test_random_slots_distinct_with_padding():
     s = workload.random_slots(100, 10, pad_fraction=0.25, seed=2)
     live = s[s >= 0]
     assert np.unique(live).size == live.size and (live < 160).all() and (s == -1).sum() > 0
+
+
+def test_mixed_step_table_fits_every_seed():
+    """The full-size mixed step's block tables hold the longest sequence any seed can draw
+    (a decode row with 8192 cached tokens plus its new one needs 513 blocks)."""
+    import inspect
+
+    width = inspect.signature(workload.configs.mixed_step_bf16).parameters["max_blocks_per_seq"].default
+    assert width * BS >= 8192 + 1
+    for seed in range(64):
+        ctx, qlen = workload.configs.mixed_step_lengths(seed)
+        assert int(((ctx + qlen + BS - 1) // BS).max()) <= width, seed
+        assert int(qlen.sum()) == 7808

@@ -38,14 +38,23 @@ def decode_batch_bf16(seed: int = 0, device="cpu", num_seqs: int = 64, lo: int =
                       seed=seed, device=device, name="decode_batch_bf16", **kw)
 
 
-def mixed_step_bf16(seed: int = 0, device="cpu", num_decode: int = 1664, ctx_lo: int = 1024,
-                    ctx_hi: int = 8192, chunk: int = 2048, chunk_ctx=(0, 2048, 6144),
-                    max_blocks_per_seq: int = 512, **kw) -> Step:
-    """1664 decode tokens (context ~ U[1024, 8192]) then three 2048-token prefill chunks whose
-    cached context is 0, 2048 and 6144 tokens: 7808 tokens under an 8192-token budget."""
+def mixed_step_lengths(seed: int = 0, num_decode: int = 1664, ctx_lo: int = 1024, ctx_hi: int = 8192,
+                       chunk: int = 2048, chunk_ctx=(0, 2048, 6144)):
+    """(context_lens, query_lens) of the mixed step: decode rows first, then the chunks."""
     ctx_dec = _lengths_rng(seed).integers(ctx_lo, ctx_hi, size=num_decode, endpoint=True)
     ctx = np.concatenate([ctx_dec, np.asarray(chunk_ctx, np.int64)])
     qlen = np.concatenate([np.ones(num_decode, np.int64), np.full(len(chunk_ctx), chunk, np.int64)])
+    return ctx, qlen
+
+
+def mixed_step_bf16(seed: int = 0, device="cpu", num_decode: int = 1664, ctx_lo: int = 1024,
+                    ctx_hi: int = 8192, chunk: int = 2048, chunk_ctx=(0, 2048, 6144),
+                    max_blocks_per_seq: int = 513, **kw) -> Step:
+    """1664 decode tokens (context ~ U[1024, 8192]) then three 2048-token prefill chunks whose
+    cached context is 0, 2048 and 6144 tokens: 7808 tokens under an 8192-token budget. The
+    block tables are 513 blocks wide, room for a decode row with 8192 cached tokens plus
+    its new one."""
+    ctx, qlen = mixed_step_lengths(seed, num_decode, ctx_lo, ctx_hi, chunk, chunk_ctx)
     return build_step(ctx, qlen, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
                       max_blocks_per_seq=max_blocks_per_seq, seed=seed, device=device,
                       name="mixed_step_bf16", **kw)
