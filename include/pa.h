@@ -142,7 +142,11 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
 
 /*
  * Bytes of device workspace pa_attention needs for these sizes (written to *bytes).
- * The figure depends only on the arguments (and on PA_KV_PARTITION, see below).
+ * The figure depends only on the arguments (and on PA_KV_PARTITION, see below). It is
+ * the planner's work lists plus an area for split-KV partial results sized by an upper
+ * bound over every step of these sizes; that bound grows with the sequences that can be
+ * split, not with the block-table width (for example 55 MB for 1667 sequences with
+ * tables 513 blocks wide, 32 query and 8 kv heads, head_dim 128).
  */
 pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq,
                                       int64_t num_tokens, int32_t num_q_heads,
@@ -192,8 +196,11 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache,
  *   info[1] = decode rows (sequences with exactly one query row)
  *   info[2] = keys of the prefix shared by all decode rows and attended once (0: none)
  *   info[3] = partitions that shared prefix was cut into
+ *   info[4] = partial-result slots the plan used (one slot = D + 2 floats); the
+ *             workspace holds an upper bound over every plan of the call's sizes
+ *   info[5] = keys per shared-prefix partition (0: no shared prefix)
  * The size arguments must be those of that pa_attention call. info is host memory
- * (4 int32). The call waits for `stream` to finish, then copies 16 bytes.
+ * (6 int32). The call waits for `stream` to finish, then copies 24 bytes.
  * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED, PA_E_WORKSPACE, PA_E_HIP.
  */
 pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, int32_t num_seqs,

@@ -86,9 +86,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int g = (int)(wg % hkv);
   const int64_t t = wg / hkv;
   if (t >= p.plan_hdr[kHdrDecTasks]) return;
-  const int task = p.dec_tasks[t];
-  const int part = task % p.max_parts;
-  const int i = task / p.max_parts;
+  const int i = p.dec_tasks[2 * t];
+  const int part = p.dec_tasks[2 * t + 1];
   const int row = p.qsl[i];
   const int L = p.seq_lens[i];
   const int P = p.part_tokens;
@@ -237,7 +236,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       *reinterpret_cast<u32x2*>(orow + dt * 16) = w;
     }
   } else {
-    const int64_t slot = part_slot(p, i, slot_part, g, c);
+    const int64_t slot = part_slot(p.part_base[i], nparts, nrows * G, g, c, slot_part);
     float* po = p.part_o + slot * D + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt];

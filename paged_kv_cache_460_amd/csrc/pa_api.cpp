@@ -176,7 +176,8 @@ int device_cus() {
   return n;
 }
 
-Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads) {
+Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int64_t num_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads) {
   const int64_t max_len = (int64_t)max_blocks * kBlock;
   const int64_t len64 = std::max<int64_t>(64, (max_len + 63) / 64 * 64);
   int64_t P = 0;
@@ -201,18 +202,37 @@ Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int32_t n
   Partitioning r;
   r.part_tokens = (int32_t)P;
   // The shared prefix is attended by few, wide tasks (all decode rows at once), so it is
-  // cut finer to give the prefix kernel enough of them.
-  r.prefix_part_tokens = (int32_t)std::min<int64_t>(P, 512);
-  // prefix partitions of the prefix length, then suffix partitions of P >= that length:
-  // at most ceil(max_len / prefix partition) + 1 of them
-  r.max_parts = (int32_t)((max_len + r.prefix_part_tokens - 1) / r.prefix_part_tokens + 1);
+  // cut finer than P, into partitions of at least this many keys (the planner takes
+  // fewer, longer ones when there are many decode rows).
+  r.prefix_part_min = (int32_t)std::min<int64_t>(P, 512);
+  const int64_t Q = (max_len + P - 1) / P;
+  r.max_task_parts = (int32_t)std::min<int64_t>(Q, INT32_MAX);
+  // Partial slots, bounded over every plan these sizes allow, in units of Hkv * G slots
+  // (one per kv head and column of a decode row). A sequence is merged when its result
+  // is split over nparts >= 2 partitions, and then holds nparts * Hkv * rows * G slots:
+  //  * its own partitions ns: a sequence split ns >= 2 ways has len > P keys, so ns <=
+  //    ceil(len / P) < 2 len / P <= 2 max_len / P, and ns <= Q; it has at most 16 / G rows
+  //    (a longer one is a prefill chunk), and all such rows together are at most T;
+  //  * a decode row with a shared prefix and a single partition of its own: one unit;
+  //  * shared-prefix partitions: the planner keeps (decode rows) x (prefix partitions)
+  //    at most max(kPrefixSlotRows, decode rows).
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t rows_max = std::max<int64_t>(1, 16 / G);
+  const int64_t seqs = std::min<int64_t>(num_seqs, num_tokens);  // sequences with rows
+  int64_t own = 0;
+  if (Q >= 2) {
+    const int64_t by_count = Q * std::min<int64_t>(num_tokens, seqs * rows_max);
+    const int64_t by_len = rows_max * ((2 * seqs * max_len + P - 1) / P);
+    own = std::min(by_count, by_len);
+  }
+  const int64_t prefix = std::max<int64_t>(kPrefixSlotRows, seqs);
+  r.part_capacity = (own + seqs + prefix) * G * num_kv_heads;
   return r;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
-                                 int32_t max_parts) {
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t head_dim, pa_dtype dtype, const Partitioning& part) {
   WorkspaceLayout w{};
   if (dtype != PA_BF16 || num_seqs == 0) return w;  // the fp32 path needs no workspace
   size_t off = 0;
@@ -221,14 +241,15 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t
   w.plan_hdr = off;
   off += align256(sizeof(int32_t) * kHdrSize);
   w.dec_tasks = off;
-  off += align256(sizeof(int32_t) * (size_t)num_seqs * (size_t)max_parts);
+  off += align256(2 * sizeof(int32_t) * (size_t)num_seqs * (size_t)part.max_task_parts);
   w.dec_seqs = off;
   off += align256(sizeof(int32_t) * (size_t)num_seqs);
-  const size_t slots = (size_t)num_seqs * (size_t)max_parts * (size_t)num_kv_heads * 16;
+  w.part_base = off;
+  off += align256(sizeof(int64_t) * (size_t)num_seqs);
   w.part_o = off;
-  off += align256(slots * (size_t)head_dim * sizeof(float));
+  off += align256((size_t)part.part_capacity * (size_t)head_dim * sizeof(float));
   w.part_ml = off;
-  off += align256(slots * 2 * sizeof(float));
+  off += align256((size_t)part.part_capacity * 2 * sizeof(float));
   w.total = off;
   return w;
 }
@@ -359,8 +380,9 @@ pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_s
   const pa_status st = check_attention_sizes(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads,
                                              num_kv_heads, head_dim, dtype);
   if (st != PA_OK) return st;
-  const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
-  *bytes = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, part.max_parts).total;
+  const pa::Partitioning part =
+      pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads);
+  *bytes = pa::workspace_layout(num_seqs, head_dim, dtype, part).total;
   return PA_OK;
 }
 
@@ -420,18 +442,20 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
     return PA_OK;
   }
 
-  const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
+  const pa::Partitioning part =
+      pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads);
   p.part_tokens = part.part_tokens;
-  p.prefix_part_tokens = part.prefix_part_tokens;
-  p.max_parts = part.max_parts;
-  // Decode tasks: at most ceil(max_len / P) suffix partitions per sequence; one workgroup
-  // per (task, kv head) pair of that bound.
-  const int64_t max_len = (int64_t)max_blocks_per_seq * pa::kBlock;
-  const int64_t pairs = (int64_t)num_seqs * ((max_len + p.part_tokens - 1) / p.part_tokens) * num_kv_heads;
-  if (pairs > INT32_MAX || (int64_t)num_seqs * p.max_parts > INT32_MAX)
+  p.prefix_part_min = part.prefix_part_min;
+  p.max_task_parts = part.max_task_parts;
+  p.part_capacity = part.part_capacity;
+  // Decode tasks: at most max_task_parts partitions per sequence; one workgroup per
+  // (task, kv head) pair of that bound.
+  const int64_t tasks = (int64_t)num_seqs * p.max_task_parts;
+  const int64_t pairs = tasks * num_kv_heads;
+  if (pairs > INT32_MAX || tasks > INT32_MAX / 2)
     return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)pairs);
   p.decode_wgs = (int32_t)pairs;
-  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, p.max_parts);
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, head_dim, dtype, part);
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", w.total, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -441,6 +465,7 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   p.plan_hdr = reinterpret_cast<int32_t*>(base + w.plan_hdr);
   p.dec_tasks = reinterpret_cast<int32_t*>(base + w.dec_tasks);
   p.dec_seqs = reinterpret_cast<int32_t*>(base + w.dec_seqs);
+  p.part_base = reinterpret_cast<int64_t*>(base + w.part_base);
   p.part_o = reinterpret_cast<float*>(base + w.part_o);
   p.part_ml = reinterpret_cast<float*>(base + w.part_ml);
 
@@ -479,8 +504,9 @@ pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, 
                                              head_dim, dtype);
   if (st != PA_OK) return st;
   if (dtype != PA_BF16 || num_seqs == 0 || num_tokens == 0) return PA_OK;  // nothing planned
-  const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
-  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, part.max_parts);
+  const pa::Partitioning part =
+      pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads);
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, head_dim, dtype, part);
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, workspace_bytes);
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -523,8 +549,9 @@ pa_status pa_step_graph_create(const void* q, const void* k, const void* v, void
       !aligned16(out))
     return fail(PA_E_ALIGN, "q, k, v, k_cache, v_cache and out must be 16-byte aligned");
   if (dtype == PA_BF16) {
-    const pa::Partitioning part = pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_kv_heads);
-    const size_t need = pa::workspace_layout(num_seqs, num_kv_heads, head_dim, dtype, part.max_parts).total;
+    const pa::Partitioning part =
+        pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads);
+    const size_t need = pa::workspace_layout(num_seqs, head_dim, dtype, part).total;
     if (!workspace || workspace_bytes < need)
       return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     if (!aligned16(workspace)) return fail(PA_E_ALIGN, "workspace must be 16-byte aligned");

@@ -43,25 +43,28 @@ struct AttnParams {
   float scale;
   // split-KV decode
   int32_t part_tokens;   // decode partition length P (multiple of 64)
-  int32_t prefix_part_tokens;  // shared-prefix partition length (<= P, multiple of 64)
-  int32_t max_parts;     // partial slots per column: ceil(MB * 16 / prefix partition) + 1
-                         // (prefix partitions, then the suffix's; see choose_partitioning)
+  int32_t prefix_part_min;  // shortest shared-prefix partition (<= P, multiple of 64)
+  int32_t max_task_parts;   // ceil(MB * 16 / P): most decode partitions of one sequence
   int32_t decode_wgs;    // decode workgroups (one wave each): a bound on (task, kv head) pairs
-  float* part_o;         // [S, Hkv, 16, max_parts, D] unnormalised partial outputs
-  float* part_ml;        // [S, Hkv, 16, max_parts, 2] running max (log2 domain) and sum
+  int64_t part_capacity; // partial slots the workspace holds (see partial_capacity)
+  float* part_o;         // [part_capacity, D] unnormalised partial outputs
+  float* part_ml;        // [part_capacity, 2] running max (log2 domain) and sum
   // work lists written by the planner
   int32_t* tile_offsets; // [S + 1] exclusive prefix of prefill tiles per sequence
-  int32_t* dec_tasks;    // [S * max_parts] decode tasks, sequence * max_parts + partition
+  int32_t* dec_tasks;    // [S * max_task_parts][2] decode tasks: (sequence, partition)
   int32_t* dec_seqs;     // [S] decode sequences in step order
+  int64_t* part_base;    // [S] first partial slot of each sequence that is merged
   int32_t* plan_hdr;     // [kHdrSize] counts and the shared prefix, see kHdr*
 };
 
-// Partial-result slot of (sequence i, partition q, kv head g, MFMA column c). The 16
-// columns of a kv head hold a partition's (row, head-in-group) pairs, c = row * G + h % G:
-// one row for a decode row, up to 16/G rows for a short multi-row sequence. A column's
-// partitions are adjacent, so the merge reads each column's partials in one run.
-__host__ __device__ inline int64_t part_slot(const AttnParams& p, int i, int q, int g, int c) {
-  return (((int64_t)i * p.num_kv_heads + g) * 16 + c) * p.max_parts + q;
+// Partials of a sequence whose decode-path result is split over nparts >= 2 partitions
+// (shared-prefix partitions first, then its own): one slot per (partition, kv head, live
+// MFMA column), in a region of nparts * Hkv * ncols slots that the planner places at
+// part_base[i]. The live columns of a kv head are its (row, head-in-group) pairs, c = row
+// * G + h % G: ncols = G for a decode row, rows * G (<= 16) for a short multi-row sequence.
+// A column's partitions are adjacent, so the merge reads each column's partials in one run.
+__host__ __device__ inline int64_t part_slot(int64_t base, int nparts, int ncols, int g, int c, int q) {
+  return base + ((int64_t)g * ncols + c) * nparts + q;
 }
 
 // Decode-path KV partitions of a range of `len` keys: n partitions of plen keys, the last
@@ -85,8 +88,17 @@ constexpr int kHdrDecTasks = 0;     // decode tasks in dec_tasks
 constexpr int kHdrDecSeqs = 1;      // decode sequences in dec_seqs
 constexpr int kHdrPrefixKeys = 2;   // keys of the shared prefix (0: none)
 constexpr int kHdrPrefixParts = 3;  // partitions the shared prefix is cut into
-constexpr int kHdrSize = 4;
-constexpr int kHdrInfo = 4;         // fields reported by pa_attention_plan_info
+constexpr int kHdrPartSlots = 4;    // partial slots the plan uses (<= part_capacity)
+constexpr int kHdrPrefixPartTokens = 5;  // keys per shared-prefix partition (multiple of 64)
+constexpr int kHdrSize = 6;
+constexpr int kHdrInfo = 6;         // fields reported by pa_attention_plan_info
+
+// Shared-prefix partitions: a partition holds at least prefix_part_min keys, and all
+// decode rows together hold at most max(kPrefixSlotRows, rows) prefix partials per
+// (kv head, column) (one partition each when there are more rows than that): the prefix
+// kernel draws its parallelism from the partitions when there are few rows, and from
+// the rows when there are many.
+constexpr int kPrefixSlotRows = 1024;
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WorkspaceLayout {
@@ -94,20 +106,22 @@ struct WorkspaceLayout {
   size_t plan_hdr;
   size_t dec_tasks;
   size_t dec_seqs;
+  size_t part_base;
   size_t part_o;
   size_t part_ml;
   size_t total;
 };
 
-// Partition lengths of a step and the partial slots they need; see choose_partitioning.
+// Partition lengths of a step and the partial slots they can need; see choose_partitioning.
 struct Partitioning {
-  int32_t part_tokens;         // decode partitions
-  int32_t prefix_part_tokens;  // shared-prefix partitions
-  int32_t max_parts;           // partial slots per (sequence, kv head, column)
+  int32_t part_tokens;      // decode partitions
+  int32_t prefix_part_min;  // shortest shared-prefix partition
+  int32_t max_task_parts;   // decode partitions of the longest sequence the tables allow
+  int64_t part_capacity;    // partial slots: an upper bound on what any plan of these sizes uses
 };
-Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads);
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
-                                 int32_t max_parts);
+Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int64_t num_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads);
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t head_dim, pa_dtype dtype, const Partitioning& part);
 int device_cus();  // CUs of the current device
 
 // Kernel launchers (defined next to their kernels). Each returns hipGetLastError().

@@ -60,6 +60,29 @@ __device__ inline int block_exclusive_scan(int32_t* wsum, int tid, int value, in
   return before + v - value;
 }
 
+// The same scan over 64-bit values (partial-slot offsets).
+__device__ inline int64_t block_exclusive_scan64(int64_t* wsum, int tid, int64_t value, int64_t& total) {
+  const int lane = tid & 63, w = tid >> 6;
+  int64_t v = value;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int64_t x = wsum[k];
+    before += k < w ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  total = all;
+  return before + v - value;
+}
+
 __device__ inline int block_min(int32_t* wsum, int tid, int value) {
   const int lane = tid & 63, w = tid >> 6;
   int v = value;
@@ -78,6 +101,7 @@ __device__ inline int block_min(int32_t* wsum, int tid, int value) {
 // The planner, run by one workgroup of 1024 threads.
 __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
   __shared__ int32_t sums[16];  // per-wave partial results of the block reductions
+  __shared__ int64_t sums64[16];
   __shared__ int32_t bcount[kBuckets];
   __shared__ int32_t bfill[kBuckets];
   __shared__ int32_t boff[kBuckets];
@@ -171,7 +195,17 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
     }
   }
   if (prefix_blocks < kMinPrefixBlocks) prefix_blocks = 0;
-  const int prefix_keys = prefix_blocks * kBlock;
+  int prefix_keys = prefix_blocks * kBlock;
+  // Shared-prefix partitions: at least prefix_part_min keys each (a multiple of 64), and
+  // at most max(kPrefixSlotRows / decode rows, 1) of them, which bounds the partials.
+  int pparts = 0, pplen = 0;
+  if (prefix_keys > 0) {
+    const int pmin = p.prefix_part_min;
+    int n = (prefix_keys + pmin - 1) / pmin;
+    n = min(n, max(1, kPrefixSlotRows / total_dec));
+    pplen = ((prefix_keys + n - 1) / n + 63) / 64 * 64;
+    pparts = (prefix_keys + pplen - 1) / pplen;
+  }
 
   // ---- decode-path tasks: partitions of each decode suffix [prefix_keys, L) and of each
   // multi-row sequence's whole range [0, L) ----
@@ -179,11 +213,21 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
     const int n = qsl[i + 1] - qsl[i];
     return n == 1 ? seq_lens[i] - prefix_keys : (is_multi(n) ? seq_lens[i] : 0);
   };
+  // Partial slots of sequence i: nparts * Hkv * live columns when its result is split
+  // over two or more partitions (shared-prefix ones included), else none.
+  const int hkv = p.num_kv_heads;
+  auto part_slots = [&](int i) -> int64_t {
+    const int n = qsl[i + 1] - qsl[i];
+    if (n != 1 && !is_multi(n)) return 0;
+    const int nparts = (n == 1 ? pparts : 0) + split_parts(task_len(i), P).n;
+    return nparts >= 2 ? (int64_t)nparts * hkv * n * G : 0;
+  };
   // Tasks of exactly P keys come first, in sequence order; the others follow in 32 length
   // buckets, longest bucket first.
   auto bucket = [&](int tlen) { return (tlen - 1) * kBuckets / P; };
   auto tlen_of = [&](const PartSplit& sp, int len, int q) { return q + 1 < sp.n ? sp.plen : len - (sp.n - 1) * sp.plen; };
   int full = 0;
+  int64_t my_slots = 0;
   for (int i = b; i < e; ++i) {
     const int len = task_len(i);
     const PartSplit sp = split_parts(len, P);
@@ -192,19 +236,28 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
       if (t == P) ++full;
       else atomicAdd(&bcount[bucket(t)], 1);
     }
+    my_slots += part_slots(i);
   }
   int total_full;
   int full_run = block_exclusive_scan(sums, tid, full, total_full);
+  int64_t total_slots;
+  int64_t slot_run = block_exclusive_scan64(sums64, tid, my_slots, total_slots);
+  // The host sizes the partial area from an upper bound over every plan of these sizes,
+  // so this cannot overflow; if it ever did, nothing on the decode path runs (its rows
+  // stay unwritten) rather than writing past the workspace.
+  const bool overflow = total_slots > p.part_capacity;
   if (tid == 0) {
     int run = total_full;
     for (int k = kBuckets - 1; k >= 0; --k) {
       boff[k] = run;
       run += bcount[k];
     }
-    p.plan_hdr[kHdrDecTasks] = run;
+    p.plan_hdr[kHdrDecTasks] = overflow ? 0 : run;
     p.plan_hdr[kHdrDecSeqs] = total_dec;
-    p.plan_hdr[kHdrPrefixKeys] = prefix_keys;
-    p.plan_hdr[kHdrPrefixParts] = (prefix_keys + p.prefix_part_tokens - 1) / p.prefix_part_tokens;
+    p.plan_hdr[kHdrPrefixKeys] = overflow ? 0 : prefix_keys;
+    p.plan_hdr[kHdrPrefixParts] = overflow ? 0 : pparts;
+    p.plan_hdr[kHdrPartSlots] = overflow ? -1 : (int)min(total_slots, (int64_t)INT32_MAX);
+    p.plan_hdr[kHdrPrefixPartTokens] = pplen;
   }
   __syncthreads();
   for (int i = b; i < e; ++i) {
@@ -213,8 +266,11 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
     for (int q = 0; q < sp.n; ++q) {
       const int t = tlen_of(sp, len, q);
       const int slot = t == P ? full_run++ : boff[bucket(t)] + atomicAdd(&bfill[bucket(t)], 1);
-      p.dec_tasks[slot] = i * p.max_parts + q;
+      p.dec_tasks[2 * slot] = i;
+      p.dec_tasks[2 * slot + 1] = q;
     }
+    p.part_base[i] = slot_run;
+    slot_run += part_slots(i);
   }
 }
 

@@ -133,8 +133,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int rest = (int)(u / hkv);
     ct = rest % n_ct;
     const int pp = rest / n_ct;
-    kbeg = pp * p.prefix_part_tokens;
-    kmax = min(pkeys, kbeg + p.prefix_part_tokens);
+    const int pplen = p.plan_hdr[kHdrPrefixPartTokens];
+    kbeg = pp * pplen;
+    kmax = min(pkeys, kbeg + pplen);
     L = pkeys;  // keys at or past the shared prefix are masked (they are not shared)
     seq_or_pp = pp;
     bt = p.block_tables + (int64_t)p.dec_seqs[0] * p.max_blocks;
@@ -444,7 +445,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if constexpr (kPrefix) {
       // partial of shared-prefix partition seq_or_pp for decode sequence dec_seqs[crow]:
       // unnormalised o, running max and weight sum (the merge kernel finishes the row)
-      const int64_t slot = part_slot(p, p.dec_seqs[crow[s]], seq_or_pp, g, col % G);
+      const int i = p.dec_seqs[crow[s]];
+      const int nparts = p.plan_hdr[kHdrPrefixParts] + split_parts(p.seq_lens[i] - L, p.part_tokens).n;
+      const int64_t slot = part_slot(p.part_base[i], nparts, G, g, col % G, seq_or_pp);
       float* po = p.part_o + slot * D + 4 * h2;
 #pragma unroll
       for (int md = 0; md < D / 32; ++md)
@@ -502,12 +505,19 @@ hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream) {
 
 hipError_t launch_prefix_bf16(const AttnParams& p, hipStream_t stream) {
   if (p.num_seqs < 2) return hipSuccess;
-  // Upper bound on the planner's shared-prefix tasks: a prefix of at most max_parts - 1
-  // partitions (it leaves every decode sequence at least its new token), R decode
-  // sequences per column tile. Workgroups past the planned tasks exit at once.
-  const int R = prefill_rows_per_tile(p.group);
-  const int64_t col_tiles = (p.num_seqs + R - 1) / R;
-  const int64_t grid = (int64_t)std::max(1, p.max_parts - 1) * col_tiles * p.num_kv_heads;
+  // Upper bound on the planner's shared-prefix tasks, pparts * ceil(rows / R) with
+  // pparts * rows <= max(kPrefixSlotRows, rows) and rows <= S:
+  //   pparts * ceil(rows / R) <= (pparts * rows + pparts * (R - 1)) / R,
+  // pparts at most the prefix (shorter than the longest sequence) over the shortest
+  // partition, and at most kPrefixSlotRows / 2 (there are at least two decode rows).
+  // Workgroups past the planned tasks exit at once.
+  const int64_t R = prefill_rows_per_tile(p.group);
+  const int64_t max_len = (int64_t)p.max_blocks * kBlock;
+  const int64_t pparts = std::min<int64_t>((max_len + p.prefix_part_min - 1) / p.prefix_part_min,
+                                           kPrefixSlotRows / 2);
+  const int64_t rows = std::min<int64_t>(p.num_seqs, p.num_tokens);
+  const int64_t tiles = (std::max<int64_t>(kPrefixSlotRows, rows) + pparts * (R - 1) + R - 1) / R;
+  const int64_t grid = tiles * p.num_kv_heads;
   if (p.head_dim == 128) {
     hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillWaves, kPrefillStrips, true>), dim3((unsigned)grid),
                        dim3(kPrefillWaves * 64), 0, stream, p);

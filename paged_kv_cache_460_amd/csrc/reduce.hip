@@ -10,7 +10,8 @@
 // row's G heads, or up to 16/G rows x G heads of a short multi-row sequence). Its four
 // waves take column groups round robin; within a wave D/4 lanes share a column: first
 // over partitions for M and the denominator, then over dimensions for the weighted sum,
-// eight partitions in flight. A column's partitions sit next to each other.
+// eight partitions in flight. A column's partitions sit next to each other, in the
+// sequence's region of the partial area (part_slot).
 #include "pa_internal.h"
 
 namespace pa {
@@ -29,6 +30,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnParams p) {
   const int nrows = p.qsl[i + 1] - row0;
   const int ncols = nrows * G;
   if (nrows < 1 || ncols > 16 || wave * kCpw >= ncols) return;  // off the decode path, or idle
+  if (p.plan_hdr[kHdrPartSlots] < 0) return;  // no plan (see the planner)
   const int P = p.part_tokens;
   const int prefix_keys = nrows == 1 ? p.plan_hdr[kHdrPrefixKeys] : 0;
   const int prefix_parts = nrows == 1 ? p.plan_hdr[kHdrPrefixParts] : 0;
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnParams p) {
   for (int c0 = wave * kCpw; c0 < ncols; c0 += 4 * kCpw) {
     const int c = c0 + cs;
     const bool cvalid = c < ncols;
-    const int64_t base = part_slot(p, i, 0, g, cvalid ? c : 0);  // partition q at base + q
+    const int64_t base = part_slot(p.part_base[i], nparts, ncols, g, cvalid ? c : 0, 0);  // partition q at base + q
 
     // M = max_q m_q and den = sum_q 2^(m_q - M) l_q, online over this lane's partitions,
     // then merged over the column's lanes. A partition in which a multi-row column saw

@@ -290,3 +290,40 @@ def test_chunk_split_matches_single_chunk():
     assert_attention_close(to_f64(split), to_f64(ref), qsl, "bf16", label="two chunks vs one")
     oracle_out = oracle_step(workload.host_arrays(full))["out"]
     assert_attention_close(to_f64(split), oracle_out, qsl, "bf16", label="two chunks vs the oracle")
+
+
+def _plan_info(step):
+    import paged_kv_cache_460_amd as pa
+
+    kc, vc = step.k_cache.clone(), step.v_cache.clone()
+    ws = torch.empty(pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, step.num_tokens,
+                                                 step.num_q_heads, step.num_kv_heads, step.head_dim, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    pa.step(step.q, step.k, step.v, kc, vc, step.block_tables, step.seq_lens, step.query_start_loc,
+            step.context_lens, step.scale, workspace=ws)
+    return pa.attention_plan_info(ws, step.q, kc, step.block_tables)
+
+
+def test_partials_at_their_bound(monkeypatch):
+    """Multi-row sequences of 16 rows (G = 1) over the whole table, cut into 64-key
+    partitions: the partial area is used up to the bound the host sizes it by."""
+    monkeypatch.setenv("PA_KV_PARTITION", "64")
+    ctx, qlen = [992] * 8, [16] * 8
+    step = workload.build_step(ctx, qlen, num_q_heads=2, num_kv_heads=2, head_dim=128, dtype="bf16", seed=12,
+                               max_blocks_per_seq=63, device=DEV, name="partials_at_bound")
+    check_full(step, "partials_at_bound")
+    info = _plan_info(step)
+    # each sequence: 1008 keys in 16 partitions of 63 -> 64 keys, 16 columns, 2 kv heads
+    assert info["decode_tasks"] == 8 * 16 and info["partial_slots"] == 8 * 16 * 2 * 16, info
+
+
+def test_shared_prefix_many_decode_rows():
+    """More decode rows than the shared-prefix partial rows allow per partition: the prefix
+    is attended in one partition, and every row still matches the oracle."""
+    S = 1100
+    suffix = [1 + (13 * i) % 40 for i in range(S)]
+    step = _shared_prefix_step(6, suffix, 4, 1, 64)
+    check_full(step, "shared_prefix/many_decode_rows")
+    info = _plan_info(step)
+    assert info["decode_rows"] == S and info["shared_prefix_keys"] == 96 and info["shared_prefix_parts"] == 1, info
+    assert info["shared_prefix_part_keys"] == 128 and info["partial_slots"] == S * 2 * 1 * 4, info
