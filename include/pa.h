@@ -190,6 +190,32 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache,
                        size_t workspace_bytes, void* stream);
 
 /*
+ * pa_attention without a workspace argument, for callers that cannot allocate device
+ * memory: code under stream capture, tight serving loops, harnesses that forbid
+ * allocation. Arguments, results, routing and errors are those of pa_attention (same
+ * kernels, bit-identical output); the workspace is instead a fixed device array of
+ * PA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the process ends.
+ * The call allocates and frees nothing. Sizes whose pa_attention_workspace_size exceeds
+ * PA_NOALLOC_SCRATCH_BYTES are rejected with PA_E_WORKSPACE before anything is enqueued
+ * (64 MiB holds, for example, 1667 sequences with tables 513 blocks wide, 32 query and 8
+ * kv heads, head_dim 128). All calls on one GPU share that GPU's array and the last
+ * call's contents stay in it (nothing in it needs clearing: each call's planner writes
+ * what its kernels read), so calls that overlap in time on one GPU, on any streams, race:
+ * order them on one stream or with events. The first call on a device looks up the
+ * array's device address (PA_E_HIP if that fails).
+ * Errors: those of pa_attention, PA_E_WORKSPACE for sizes beyond the scratch.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+pa_status pa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, const int32_t* context_lens,
+                               float scale, void* out, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int64_t num_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                               pa_dtype dtype, void* stream);
+
+/*
  * What the on-device planner decided in the last pa_attention call that used this
  * workspace (bf16 steps; the fp32 path plans nothing and leaves info untouched):
  *   info[0] = decode (sequence, KV partition) tasks

@@ -11,6 +11,7 @@ from .ops import (
     PAError,
     StepGraph,
     attention,
+    attention_noalloc,
     attention_plan_info,
     attention_workspace_size,
     build_slot_mapping,
@@ -29,6 +30,7 @@ __all__ = [
     "PAError",
     "StepGraph",
     "attention",
+    "attention_noalloc",
     "attention_plan_info",
     "attention_workspace_size",
     "build_slot_mapping",

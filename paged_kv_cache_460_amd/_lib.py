@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32, PA_BF16 = 0, 1
 BLOCK_SIZE = 16
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 STATUS_NAMES = {
     0: "PA_OK",
@@ -50,6 +51,8 @@ _SIGNATURES = {
                                                    ctypes.POINTER(ctypes.c_size_t)]),
     "pa_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I64, _I32,
                                     _I32, _I32, _I64, ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "pa_attention_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I64,
+                                            _I32, _I32, _I32, _I64, ctypes.c_int, _P]),
     "pa_attention_plan_info": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
                                               ctypes.POINTER(_I32), _P]),
     "pa_step_graph_create": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I32,

@@ -33,6 +33,7 @@ SOURCES = [
     "prefill_bf16.hip",
     "attn_f32.hip",
     "debug_checks.hip",
+    "noalloc.hip",
 ]
 
 ARCH = "gfx950"

@@ -157,6 +157,36 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cont
     return out
 
 
+def attention_noalloc(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out):
+    """``attention`` into a caller-provided ``out`` with the library's fixed scratch as the
+    workspace (pa_attention_noalloc in pa.h): the library allocates nothing. Sizes needing
+    more than ``NOALLOC_SCRATCH_BYTES`` of workspace raise PAError (PA_E_WORKSPACE)."""
+    lib = _lib.load()
+    dev = q.device
+    _need(q, "q", ndim=3)
+    dt = _payload_dtype(q, "q")
+    _need(k_cache, "k_cache", q.dtype, 4, dev)
+    _need(v_cache, "v_cache", q.dtype, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(out, "out", q.dtype, 3, dev)
+    T, hq, d = q.shape
+    nb, hkv = k_cache.shape[0], k_cache.shape[1]
+    S, MB = block_tables.shape
+    if tuple(k_cache.shape) != (nb, hkv, _lib.BLOCK_SIZE, d) or tuple(v_cache.shape) != (nb, hkv, d, _lib.BLOCK_SIZE):
+        raise ValueError("caches must be [NB, Hkv, 16, D] (keys) and [NB, Hkv, D, 16] (values)")
+    if seq_lens.shape[0] != S or context_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("seq_lens/context_lens must be [S] and query_start_loc [S+1]")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check(lib.pa_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+                                    _ptr(query_start_loc), _ptr(context_lens), float(scale), _ptr(out), S, MB, T,
+                                    hq, hkv, d, nb, dt, _stream(q)))
+    return out
+
+
 def attention_plan_info(workspace, q, k_cache, block_tables):
     """The on-device planner's summary of the last ``attention`` call that used
     ``workspace`` with these tensors' sizes (see pa_attention_plan_info in pa.h)."""
