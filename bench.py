@@ -13,9 +13,13 @@ over 8 kv heads, head dim 128, bf16, 16-token blocks): the one workload that exe
 every kernel of the path. Inputs are seeded synthetic draws, resident in HBM before the
 timed region starts.
 
-Prints one JSON line with the whole-step rate (tokens/s), the decode kernel's HBM
-roofline figures, the prefill kernel's MFMA utilisation, and the CPU oracle's rate on a
-bounded sample of the same step.
+Prints one JSON line with the whole-step rate (tokens/s) and, from per-kernel HIP-event
+durations of eager steps: the dominant kernel's roofline (decode: KV bytes it reads per
+launch / its duration, against HBM peak; prefill: causal flops / duration, against bf16
+MFMA peak); the decode side's KV rate over t_dec = plan + shared-prefix + decode + merge
+time, logical (every decode-path sequence's tokens) and unique (each physical block
+once), warm (steps back to back) and cold (1 GiB read before each step); and the CPU
+oracle's rate on a bounded sample of the same step.
 """
 
 from __future__ import annotations
@@ -40,19 +44,45 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def step_work(step):
-    """Algorithmic work of one step: decode KV bytes, prefill flops, scatter bytes."""
+def step_work(step, prefix_keys=0):
+    """Algorithmic work of one step, with its rows classified as the planner does.
+
+    A sequence of one row is a decode row; one of n >= 2 rows with n * G <= 16 (a short
+    speculative-verification sequence) also takes the decode path; longer ones are
+    prefill chunks. `prefix_keys` is the shared prefix the planner found (its keys are
+    read by the shared-prefix kernel, once for all decode rows).
+    """
     ctx, qlen, L = step.lengths()
     e = 2 if step.dtype == "bf16" else 4
     hkv, hq, d = step.num_kv_heads, step.num_q_heads, step.head_dim
-    dec = qlen == 1
-    kv_bytes = int((L[dec] * hkv * d * 2 * e).sum())
-    ch = qlen >= 2
+    G = hq // hkv
+    dec = (qlen == 1) | ((qlen >= 2) & (qlen * G <= 16))
+    ch = (qlen >= 2) & (qlen * G > 16)
+    tok_bytes = hkv * d * 2 * e  # K and V of one token, all kv heads
+    # logical KV bytes: every decode-path sequence's valid tokens
+    logical = int(L[dec].sum()) * tok_bytes
+    # unique KV bytes: each physical block counted once, with the most tokens any
+    # decode-path sequence reads from it
+    bt = step.block_tables.cpu().numpy()
+    fill = {}
+    for i in np.nonzero(dec)[0]:
+        nb = (int(L[i]) + 15) // 16
+        for b in range(nb):
+            phys = int(bt[i, b])
+            fill[phys] = max(fill.get(phys, 0), min(16, int(L[i]) - 16 * b))
+    unique = int(sum(fill.values())) * tok_bytes
+    # what the decode kernel itself reads: a decode row's suffix past the shared prefix
+    single = qlen == 1
+    decode_kernel = logical - (int(single.sum()) * prefix_keys * tok_bytes if prefix_keys else 0)
     pairs = int((qlen[ch] * ctx[ch] + qlen[ch] * (qlen[ch] + 1) // 2).sum())
     prefill_flops = 4 * d * hq * pairs
-    scatter_bytes = int(qlen.sum()) * hkv * d * 2 * e * 2  # read + write, K and V
-    return {"decode_kv_bytes": kv_bytes, "decode_rows": int(dec.sum()), "prefill_flops": prefill_flops,
-            "prefill_causal_pairs_per_head": pairs, "scatter_bytes": scatter_bytes}
+    prefix_flops = 4 * d * hq * int(single.sum()) * prefix_keys if prefix_keys else 0
+    scatter_bytes = int(qlen.sum()) * tok_bytes * 2  # read + write, K and V
+    return {"decode_kv_bytes": logical, "decode_kv_unique_bytes": unique, "decode_kernel_kv_bytes": decode_kernel,
+            "decode_rows": int(single.sum()), "decode_path_seqs": int(dec.sum()), "chunk_seqs": int(ch.sum()),
+            "prefill_flops": prefill_flops, "prefill_causal_pairs_per_head": pairs,
+            "prefix_keys": int(prefix_keys), "prefix_flops": prefix_flops,
+            "prefix_kv_bytes": int(prefix_keys) * tok_bytes, "scatter_bytes": scatter_bytes}
 
 
 def profiled_traffic(workload_name):
@@ -84,11 +114,15 @@ def profiled_traffic(workload_name):
 
 
 def cpu_baseline(step, frac):
-    """The CPU oracle, as it stands, on every k-th row of the same step."""
+    """The CPU oracle, as it stands, on every k-th row of the same step, with numpy's BLAS
+    on the host cores this process may use (capped by OMP_NUM_THREADS when that is set)."""
     import oracle
     import workload
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
+    affinity = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(affinity, cap) if cap > 0 else affinity
     T = step.num_tokens
     stride = max(1, int(round(1.0 / frac)))
     rows = np.arange(0, T, stride)
@@ -100,14 +134,15 @@ def cpu_baseline(step, frac):
     sub_qsl = a["query_start_loc"]
     pos_in_sub = {int(s): j for j, s in enumerate(seqs)}
     sub_rows = np.array([sub_qsl[pos_in_sub[int(s)]] + (r - qsl[s]) for r, s in zip(rows, seq_of)])
-    t0 = time.perf_counter()
-    _, slots = oracle.slot_mapping(a["block_tables"], a["query_start_loc"], a["context_lens"])
-    kc, vc = oracle.reshape_and_cache(a["k"], a["v"], a["k_cache"], a["v_cache"], slots)
-    oracle.attention(a["q"], kc, vc, a["block_tables"], a["seq_lens"], a["query_start_loc"], a["context_lens"],
-                     a["scale"], rows=sub_rows)
-    secs = time.perf_counter() - t0
-    pools = threadpool_info()
-    threads = max([p.get("num_threads", 1) for p in pools] + [1])
+    with threadpool_limits(limits=threads):
+        pools = threadpool_info()
+        t0 = time.perf_counter()
+        _, slots = oracle.slot_mapping(a["block_tables"], a["query_start_loc"], a["context_lens"])
+        kc, vc = oracle.reshape_and_cache(a["k"], a["v"], a["k_cache"], a["v_cache"], slots)
+        oracle.attention(a["q"], kc, vc, a["block_tables"], a["seq_lens"], a["query_start_loc"], a["context_lens"],
+                         a["scale"], rows=sub_rows)
+        secs = time.perf_counter() - t0
+    used = max([p.get("num_threads", 1) for p in pools] + [1])
     blas = ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in pools})) or "unknown"
     cpu_model = "unknown"
     try:
@@ -120,14 +155,19 @@ def cpu_baseline(step, frac):
     return {
         "value": len(rows) / secs,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": int(used),
+        "affinity_cpus": affinity,
         "cpu_model": cpu_model,
         "blas": blas,
         "kind": "oracle",
         "sample": f"every {stride}th row of the step ({len(rows)} of {T} rows, {len(seqs)} sequences), "
-                  f"fp64 numpy; cache write + attention for those rows; {secs:.1f} s",
+                  f"fp64 numpy; slot mapping, cache write and attention for those rows; {secs:.1f} s",
         "seconds": secs,
     }
+
+
+# Oracle sample per workload: about 10-30 s of host work on the GPU machine.
+CPU_SAMPLE_FRAC = {"mixed_step_bf16": 1.0 / 3}
 
 
 def main():
@@ -140,7 +180,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as separate launches instead of one HIP-graph replay")
-    ap.add_argument("--cpu-sample-frac", type=float, default=1.0 / 3)
+    ap.add_argument("--cpu-sample-frac", type=float, default=None,
+                    help="fraction of the step's rows the oracle computes (default: per workload)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="scratch read between the steps of the cold-cache pass (0: no cold pass)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -164,7 +207,6 @@ def main():
 
     log(f"[bench] building workload {args.workload} (seed {args.seed}) on {dev}")
     step = workload.make_config(args.workload, seed=args.seed, device=dev)
-    work = step_work(step)
     T = step.num_tokens
     ws = torch.empty(max(1, pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, T, step.num_q_heads,
                                                         step.num_kv_heads, step.head_dim, step.q.dtype)),
@@ -217,24 +259,113 @@ def main():
 
     # Per-kernel durations: K eager steps with every launch bracketed by HIP events on its
     # own stream (libpa's timing); a graph replay runs these same kernels.
+    kinds = ("slot_mapping", "scatter", "plan", "prefix", "decode", "reduce", "prefill", "attn_f32")
+
+    def attention_call():
+        pa.attention(step.q, step.k_cache, step.v_cache, step.block_tables, step.seq_lens, step.query_start_loc,
+                     step.context_lens, step.scale, out=out, workspace=ws)
+
+    def cool(flush):
+        # Reading 1 GiB evicts every cache level (L2 8 x 4 MB, MALL 256 MB) and leaves only
+        # clean lines; a write would leave dirty lines whose write-back lands in the next
+        # step's decode.
+        if flush is not None:
+            torch.sum(flush[0], dim=0, out=flush[1])
+
+    def timed_eager(flush=None):
+        with pa.KernelTimer() as timer:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                cool(flush)
+                run_step()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / args.steps
+            kernels = {k: timer.read(k) for k in kinds}
+        return ms, {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kernels.items()}
+
+    def attention_spans(flush=None):
+        """Mean GPU time of whole attention calls (plan, prefix, decode, merge, prefill),
+        one event pair around each, without libpa's per-kernel events."""
+        marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for a, b in marks:
+            cool(flush)
+            _, sm = pa.build_slot_mapping(step.block_tables, step.query_start_loc, step.context_lens, num_tokens=T,
+                                          with_positions=False)
+            pa.reshape_and_cache(step.k, step.v, step.k_cache, step.v_cache, sm)
+            a.record()
+            attention_call()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in marks) / len(marks)
+
     log(f"[bench] timing {args.steps} eager steps with per-kernel events")
-    with pa.KernelTimer() as timer:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            run_step()
-        torch.cuda.synchronize()
-        eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        kernels = {k: timer.read(k) for k in ("slot_mapping", "scatter", "plan", "prefix", "decode", "reduce",
-                                              "prefill", "attn_f32")}
-    avg_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kernels.items()}
+    eager_ms_per_step, avg_ms = timed_eager()
     log(f"[bench] eager {eager_ms_per_step:.3f} ms/step; kernel averages (ms): "
         + ", ".join(f"{k}={v:.4f}" for k, v in avg_ms.items() if v))
+    span_ms = attention_spans()
+    cold_ms = cold_span_ms = None
+    if args.flush_mib > 0:
+        flush = (torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device=dev),
+                 torch.zeros((), dtype=torch.float32, device=dev))
+        log(f"[bench] timing {args.steps} eager steps, {args.flush_mib} MiB read before each (cold caches)")
+        _, cold_ms = timed_eager(flush)
+        cold_span_ms = attention_spans(flush)
+        del flush
+        log("[bench] cold kernel averages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in cold_ms.items() if v))
 
-    dec_ms = avg_ms["decode"]
-    dec_gbps = work["decode_kv_bytes"] / (dec_ms * 1e-3) / 1e9 if dec_ms else None
-    pre_ms = avg_ms["prefill"]
-    pre_tflops = work["prefill_flops"] / (pre_ms * 1e-3) / 1e12 if pre_ms and work["prefill_flops"] else None
+    # What the planner decided (the shared prefix it found), then the step's algorithmic work.
+    prefix_keys = 0
+    if step.dtype == "bf16":
+        prefix_keys = pa.attention_plan_info(ws, step.q, step.k_cache, step.block_tables)["shared_prefix_keys"]
+    work = step_work(step, prefix_keys)
+
+    def rates(ms, span):
+        """Decode-side GB/s and the MFMA kernels' rates from per-kernel averages (ms).
+
+        t_dec is the GPU time of the planner, shared-prefix, decode and merge launches: the
+        sum of their event-bracketed durations, or, in a step without prefill chunks, the
+        whole attention call's span (the same launches plus an empty prefill one), which
+        is free of the per-launch event overhead."""
+        t_events = ms["plan"] + ms["prefix"] + ms["decode"] + ms["reduce"]
+        t_dec = span if work["chunk_seqs"] == 0 and span else t_events
+        gbps = lambda b, t: b / (t * 1e-3) / 1e9 if t and b else None
+        tflops = lambda f, t: f / (t * 1e-3) / 1e12 if t and f else None
+        r = {
+            "t_dec_ms": t_dec,
+            "t_dec_events_ms": t_events,
+            "attention_span_ms": span,
+            "decode_kv_gbps": gbps(work["decode_kv_bytes"], t_dec),
+            "decode_kv_unique_gbps": gbps(work["decode_kv_unique_bytes"], t_dec),
+            "decode_kernel_gbps": gbps(work["decode_kernel_kv_bytes"], ms["decode"]),
+            "prefill_tflops": tflops(work["prefill_flops"], ms["prefill"]),
+            "prefix_tflops": tflops(work["prefix_flops"], ms["prefix"]),
+        }
+        for k in ("decode_kv_gbps", "decode_kv_unique_gbps", "decode_kernel_gbps"):
+            r[k.replace("gbps", "hbm_frac")] = r[k] / HBM_PEAK_GBPS if r[k] else None
+        for k in ("prefill", "prefix"):
+            t = r[f"{k}_tflops"]
+            r[f"{k}_mfma_util"] = t / BF16_MFMA_PEAK_TFLOPS if t else None
+        return r
+
+    warm = rates(avg_ms, span_ms)
+    cold = rates(cold_ms, cold_span_ms) if cold_ms else None
+    # The dominant kernel (longest average launch) and its roofline: bytes for the
+    # bandwidth-bound decode kernel, flops for the matrix-core kernels.
+    dominant = max(("decode", "prefill", "prefix", "attn_f32"), key=lambda k: avg_ms[k])
+    if dominant == "decode":
+        roof = {"bound": "hbm", "kernel": "decode", "achieved": warm["decode_kernel_gbps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "algorithmic_bytes_per_launch": work["decode_kernel_kv_bytes"]}
+    elif dominant in ("prefill", "prefix"):
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": warm[f"{dominant}_tflops"],
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "algorithmic_flops_per_launch": work[f"{dominant}_flops"]}
+    else:
+        roof = {"bound": "alu", "kernel": dominant, "achieved": None, "peak": None, "unit": None}
+    roof["frac"] = roof["achieved"] / roof["peak"] if roof["achieved"] and roof["peak"] else None
+    roof["traffic"] = profiled_traffic(args.workload) if dominant == "decode" else None
+    roof["avg_launch_ms"] = avg_ms[dominant]
 
     result = {
         "metric": METRIC,
@@ -254,6 +385,9 @@ def main():
             "num_seqs": step.num_seqs,
             "tokens_per_step": T,
             "decode_rows": work["decode_rows"],
+            "decode_path_seqs": work["decode_path_seqs"],
+            "chunk_seqs": work["chunk_seqs"],
+            "shared_prefix_keys": work["prefix_keys"],
             "num_q_heads": step.num_q_heads,
             "num_kv_heads": step.num_kv_heads,
             "head_dim": step.head_dim,
@@ -262,29 +396,26 @@ def main():
             "seed": args.seed,
             "execution": mode,
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "decode",
-            "achieved": dec_gbps,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": dec_gbps / HBM_PEAK_GBPS if dec_gbps else None,
-            "traffic": profiled_traffic(args.workload),
-            "algorithmic_bytes_per_launch": work["decode_kv_bytes"],
-            "avg_launch_ms": dec_ms,
-        },
+        "roofline": roof,
         "breakdown": {
             "kernel_avg_ms": avg_ms,
-            "decode_kv_gbps": dec_gbps,
-            "decode_hbm_frac": dec_gbps / HBM_PEAK_GBPS if dec_gbps else None,
-            "prefill_tflops": pre_tflops,
-            "prefill_mfma_util": pre_tflops / BF16_MFMA_PEAK_TFLOPS if pre_tflops else None,
+            "kernel_avg_ms_cold": cold_ms,
+            "warm": warm,
+            "cold": cold,
+            "decode_kv_bytes": work["decode_kv_bytes"],
+            "decode_kv_unique_bytes": work["decode_kv_unique_bytes"],
+            "decode_kernel_kv_bytes": work["decode_kernel_kv_bytes"],
             "prefill_flops_per_launch": work["prefill_flops"],
+            "prefix_flops_per_launch": work["prefix_flops"],
             "scatter_bytes_per_launch": work["scatter_bytes"],
+            "decode_kv_gbps": warm["decode_kv_gbps"],
+            "decode_hbm_frac": warm["decode_kv_hbm_frac"],
+            "prefill_mfma_util": warm["prefill_mfma_util"],
             "execution": mode,
             "ms_per_step_median": step_median,
             "ms_per_step_min": step_min,
             "eager_ms_per_step_with_kernel_events": eager_ms_per_step,
+            "flush_mib": args.flush_mib,
         },
     }
     if args.copy_probe_mib > 0:
@@ -298,7 +429,8 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a sample of the step)")
-        result["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_frac)
+        frac = args.cpu_sample_frac if args.cpu_sample_frac else CPU_SAMPLE_FRAC.get(args.workload, 1.0)
+        result["cpu_baseline"] = cpu_baseline(step, frac)
     print(json.dumps(result), flush=True)
 
 

@@ -145,8 +145,8 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
  * The figure depends only on the arguments (and on PA_KV_PARTITION, see below). It is
  * the planner's work lists plus an area for split-KV partial results sized by an upper
  * bound over every step of these sizes; that bound grows with the sequences that can be
- * split, not with the block-table width (for example 55 MB for 1667 sequences with
- * tables 513 blocks wide, 32 query and 8 kv heads, head_dim 128).
+ * split, not with the block-table width (for example 85 MiB for 1667 sequences with
+ * tables 513 or 8192 blocks wide, 32 query and 8 kv heads, head_dim 128).
  */
 pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq,
                                       int64_t num_tokens, int32_t num_q_heads,
@@ -174,10 +174,12 @@ pa_status pa_attention_workspace_size(int32_t num_seqs, int32_t max_blocks_per_s
  * that shared prefix attended once for all of them together; the result is the same up
  * to rounding (requests sharing cached prefix blocks: shengyayun.com blog, 关键实现细节
  * item 2).
- * Environment: PA_KV_PARTITION=<tokens> (a multiple of 64 in [64, 65536]) overrides
- * the split-KV partition length P that decode rows use: a decode-path range of len keys
- * is cut into ceil(len / P) partitions of about equal length (whole 32-key steps, at
- * most P keys each).
+ * Split-KV partitions: a decode-path range of len keys is cut into ceil(len / P)
+ * partitions of about equal length (whole 32-key steps, at most P keys each). The planner
+ * chooses P on the device from the step's actual lengths: the decode-path keys times
+ * Hkv, spread over one task per decode wave slot of the GPU (8 per CU), in whole 32-key
+ * steps and at least 256 keys; a sequence shorter than P stays whole.
+ * Environment: PA_KV_PARTITION=<tokens> (a multiple of 64 in [64, 65536]) fixes P instead.
  * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED, PA_E_ALIGN,
  * PA_E_WORKSPACE, PA_E_HIP.
  */
@@ -197,15 +199,15 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache,
  * PA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the process ends.
  * The call allocates and frees nothing. Sizes whose pa_attention_workspace_size exceeds
  * PA_NOALLOC_SCRATCH_BYTES are rejected with PA_E_WORKSPACE before anything is enqueued
- * (64 MiB holds, for example, 1667 sequences with tables 513 blocks wide, 32 query and 8
- * kv heads, head_dim 128). All calls on one GPU share that GPU's array and the last
+ * (128 MiB holds, for example, 1667 sequences with tables 513 blocks wide, 32 query and
+ * 8 kv heads, head_dim 128). All calls on one GPU share that GPU's array and the last
  * call's contents stay in it (nothing in it needs clearing: each call's planner writes
  * what its kernels read), so calls that overlap in time on one GPU, on any streams, race:
  * order them on one stream or with events. The first call on a device looks up the
  * array's device address (PA_E_HIP if that fails).
  * Errors: those of pa_attention, PA_E_WORKSPACE for sizes beyond the scratch.
  */
-#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 pa_status pa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* seq_lens,
@@ -225,8 +227,9 @@ pa_status pa_attention_noalloc(const void* q, const void* k_cache, const void* v
  *   info[4] = partial-result slots the plan used (one slot = D + 2 floats); the
  *             workspace holds an upper bound over every plan of the call's sizes
  *   info[5] = keys per shared-prefix partition (0: no shared prefix)
+ *   info[6] = decode partition length P the plan used
  * The size arguments must be those of that pa_attention call. info is host memory
- * (6 int32). The call waits for `stream` to finish, then copies 24 bytes.
+ * (7 int32). The call waits for `stream` to finish, then copies 28 bytes.
  * Errors: PA_E_NULL, PA_E_DTYPE, PA_E_SHAPE, PA_E_UNSUPPORTED, PA_E_WORKSPACE, PA_E_HIP.
  */
 pa_status pa_attention_plan_info(const void* workspace, size_t workspace_bytes, int32_t num_seqs,

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32, PA_BF16 = 0, 1
 BLOCK_SIZE = 16
-NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 STATUS_NAMES = {
     0: "PA_OK",

@@ -23,7 +23,10 @@
 //  * masked keys are removed by select (-inf score, zeroed value), never by multiplying,
 //    so unwritten slots that hold NaN cannot leak;
 //  * a sequence with a single partition writes its output row directly; otherwise the
-//    wave writes (o, m, l) partials and pa::reduce merges them.
+//    wave writes (o, m, l) partials and pa::reduce merges them. (Merging in the decode
+//    wave that finishes a sequence's last partition needs a device-scope release and
+//    acquire per wave, which here write back and invalidate the L2: decode took twice
+//    as long on a 64-row batch, so the merge stays a launch of its own.)
 #include "pa_internal.h"
 
 namespace pa {
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int part = p.dec_tasks[2 * t + 1];
   const int row = p.qsl[i];
   const int L = p.seq_lens[i];
-  const int P = p.part_tokens;
+  const int P = p.plan_hdr[kHdrPartTokens];
   const int G = p.group;
   const int hq = p.num_q_heads;
   // A task is one KV partition of a decode row or of a short multi-row sequence

@@ -179,51 +179,48 @@ int device_cus() {
 Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int64_t num_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads) {
   const int64_t max_len = (int64_t)max_blocks * kBlock;
-  const int64_t len64 = std::max<int64_t>(64, (max_len + 63) / 64 * 64);
-  int64_t P = 0;
+  int64_t fixed = 0;
   if (const char* env = std::getenv("PA_KV_PARTITION")) {
     const long v = std::strtol(env, nullptr, 10);
-    if (v >= 64 && v <= 65536 && v % 64 == 0) P = v;
-  }
-  if (P == 0) {
-    // A decode task is one (sequence, partition, kv head) streamed by one wave. Every
-    // task pays a start-up latency before it streams, so few long tasks beat many short
-    // ones, as long as there are enough of them to draw the full HBM rate: aim for one
-    // task per decode wave slot (8 per CU) if every sequence had the longest length the
-    // block table allows, and cut no partition shorter than 256 tokens or longer than
-    // that length.
-    const int64_t pairs = std::max<int64_t>(1, (int64_t)num_seqs * num_kv_heads);
-    const int64_t target = (int64_t)device_cus() * 8;
-    P = (pairs * max_len + target - 1) / target;
-    P = (P + 63) / 64 * 64;
-    P = std::min<int64_t>(std::max<int64_t>(P, 256), std::max<int64_t>(256, len64));
-    P = std::min<int64_t>(P, 1 << 24);
+    if (v >= 64 && v <= 65536 && v % 64 == 0) fixed = v;
   }
   Partitioning r;
-  r.part_tokens = (int32_t)P;
-  // The shared prefix is attended by few, wide tasks (all decode rows at once), so it is
-  // cut finer than P, into partitions of at least this many keys (the planner takes
-  // fewer, longer ones when there are many decode rows).
-  r.prefix_part_min = (int32_t)std::min<int64_t>(P, 512);
-  const int64_t Q = (max_len + P - 1) / P;
-  r.max_task_parts = (int32_t)std::min<int64_t>(Q, INT32_MAX);
-  // Partial slots, bounded over every plan these sizes allow, in units of Hkv * G slots
-  // (one per kv head and column of a decode row). A sequence is merged when its result
-  // is split over nparts >= 2 partitions, and then holds nparts * Hkv * rows * G slots:
-  //  * its own partitions ns: a sequence split ns >= 2 ways has len > P keys, so ns <=
-  //    ceil(len / P) < 2 len / P <= 2 max_len / P, and ns <= Q; it has at most 16 / G rows
-  //    (a longer one is a prefill chunk), and all such rows together are at most T;
-  //  * a decode row with a shared prefix and a single partition of its own: one unit;
-  //  * shared-prefix partitions: the planner keeps (decode rows) x (prefix partitions)
-  //    at most max(kPrefixSlotRows, decode rows).
+  r.part_tokens = (int32_t)fixed;
+  r.num_kv_heads = num_kv_heads;
+  // A decode task is one (sequence, partition, kv head) streamed by one wave. Every task
+  // pays a start-up latency before it streams, so few long tasks beat many short ones, as
+  // long as there are enough of them to draw the full HBM rate: the planner aims for one
+  // task per decode wave slot (8 per CU), all about equally long.
+  const int64_t slots = (int64_t)device_cus() * 8;
+  r.decode_slots = (int32_t)slots;
+  // Bounds over every plan of these sizes. A decode-path sequence of len <= max_len keys
+  // is cut into ns = ceil(len / plen) <= ceil(len / P) partitions. With P fixed that is
+  // at most Q = ceil(max_len / P). With P chosen by the planner, P >= 256 and P >= (sum
+  // of lengths) * Hkv / slots, so all sequences together have at most slots / Hkv + S.
   const int64_t G = num_q_heads / num_kv_heads;
   const int64_t rows_max = std::max<int64_t>(1, 16 / G);
   const int64_t seqs = std::min<int64_t>(num_seqs, num_tokens);  // sequences with rows
+  const int64_t pmin = fixed ? fixed : kMinPartTokens;
+  const int64_t Q = (max_len + pmin - 1) / pmin;
+  int64_t tasks = seqs * Q;
+  if (!fixed) tasks = std::min<int64_t>(tasks, (slots + num_kv_heads - 1) / num_kv_heads + seqs);
+  r.max_tasks = (int32_t)std::min<int64_t>(std::max<int64_t>(tasks, 1), INT32_MAX);
+  // Partial slots, in units of Hkv * G slots (one per kv head and column of a decode
+  // row). A sequence is merged when its result is split over nparts >= 2 partitions, and
+  // then holds nparts * Hkv * rows * G slots:
+  //  * its own partitions ns: split two or more ways, it has len > P keys, so ns <
+  //    2 len / P; it has at most 16 / G rows (a longer one is a prefill chunk), and all
+  //    such rows together are at most T. With P fixed, 2 len / P <= 2 max_len / P; with
+  //    P chosen by the planner, the sum of 2 len / P over sequences is at most
+  //    2 slots / Hkv;
+  //  * a decode row with a shared prefix and a single partition of its own: one unit;
+  //  * shared-prefix partitions: the planner keeps (decode rows) x (prefix partitions)
+  //    at most max(kPrefixSlotRows, decode rows).
   int64_t own = 0;
   if (Q >= 2) {
-    const int64_t by_count = Q * std::min<int64_t>(num_tokens, seqs * rows_max);
-    const int64_t by_len = rows_max * ((2 * seqs * max_len + P - 1) / P);
-    own = std::min(by_count, by_len);
+    own = Q * std::min<int64_t>(num_tokens, seqs * rows_max);
+    own = std::min(own, fixed ? rows_max * ((2 * seqs * max_len + fixed - 1) / fixed)
+                              : rows_max * ((2 * slots + num_kv_heads - 1) / num_kv_heads));
   }
   const int64_t prefix = std::max<int64_t>(kPrefixSlotRows, seqs);
   r.part_capacity = (own + seqs + prefix) * G * num_kv_heads;
@@ -241,7 +238,7 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t head_dim, pa_dtype dt
   w.plan_hdr = off;
   off += align256(sizeof(int32_t) * kHdrSize);
   w.dec_tasks = off;
-  off += align256(2 * sizeof(int32_t) * (size_t)num_seqs * (size_t)part.max_task_parts);
+  off += align256(2 * sizeof(int32_t) * (size_t)part.max_tasks);
   w.dec_seqs = off;
   off += align256(sizeof(int32_t) * (size_t)num_seqs);
   w.part_base = off;
@@ -445,15 +442,16 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   const pa::Partitioning part =
       pa::choose_partitioning(num_seqs, max_blocks_per_seq, num_tokens, num_q_heads, num_kv_heads);
   p.part_tokens = part.part_tokens;
-  p.prefix_part_min = part.prefix_part_min;
-  p.max_task_parts = part.max_task_parts;
+  p.decode_slots = part.decode_slots;
+  p.max_tasks = part.max_tasks;
   p.part_capacity = part.part_capacity;
-  // Decode tasks: at most max_task_parts partitions per sequence; one workgroup per
-  // (task, kv head) pair of that bound.
-  const int64_t tasks = (int64_t)num_seqs * p.max_task_parts;
-  const int64_t pairs = tasks * num_kv_heads;
-  if (pairs > INT32_MAX || tasks > INT32_MAX / 2)
-    return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)pairs);
+  // The planner counts partials in 32-bit units of Hkv * G slots.
+  if (part.part_capacity / ((int64_t)num_q_heads) > INT32_MAX)
+    return fail(PA_E_SHAPE, "step too large: %lld partial slots", (long long)part.part_capacity);
+  // One decode workgroup per (task, kv head) pair of the task bound; those past the
+  // planner's tasks exit at once.
+  const int64_t pairs = (int64_t)p.max_tasks * num_kv_heads;
+  if (pairs > INT32_MAX) return fail(PA_E_SHAPE, "decode grid of %lld workgroups too large", (long long)pairs);
   p.decode_wgs = (int32_t)pairs;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, head_dim, dtype, part);
   if (!workspace || workspace_bytes < w.total)

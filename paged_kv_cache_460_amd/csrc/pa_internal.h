@@ -42,16 +42,17 @@ struct AttnParams {
   int64_t num_blocks;
   float scale;
   // split-KV decode
-  int32_t part_tokens;   // decode partition length P (multiple of 64)
-  int32_t prefix_part_min;  // shortest shared-prefix partition (<= P, multiple of 64)
-  int32_t max_task_parts;   // ceil(MB * 16 / P): most decode partitions of one sequence
-  int32_t decode_wgs;    // decode workgroups (one wave each): a bound on (task, kv head) pairs
-  int64_t part_capacity; // partial slots the workspace holds (see partial_capacity)
+  int32_t part_tokens;   // decode partition length P fixed by the caller, or 0: the
+                         // planner chooses it from the step's lengths (see plan.hip)
+  int32_t decode_slots;  // (kv head, partition) tasks the planner aims to fill
+  int32_t max_tasks;     // bound on the planner's decode tasks (task list length)
+  int32_t decode_wgs;    // decode workgroups (one wave each): max_tasks * Hkv
+  int64_t part_capacity; // partial slots the workspace holds (see choose_partitioning)
   float* part_o;         // [part_capacity, D] unnormalised partial outputs
   float* part_ml;        // [part_capacity, 2] running max (log2 domain) and sum
   // work lists written by the planner
   int32_t* tile_offsets; // [S + 1] exclusive prefix of prefill tiles per sequence
-  int32_t* dec_tasks;    // [S * max_task_parts][2] decode tasks: (sequence, partition)
+  int32_t* dec_tasks;    // [max_tasks][2] decode tasks: (sequence, partition)
   int32_t* dec_seqs;     // [S] decode sequences in step order
   int64_t* part_base;    // [S] first partial slot of each sequence that is merged
   int32_t* plan_hdr;     // [kHdrSize] counts and the shared prefix, see kHdr*
@@ -90,10 +91,14 @@ constexpr int kHdrPrefixKeys = 2;   // keys of the shared prefix (0: none)
 constexpr int kHdrPrefixParts = 3;  // partitions the shared prefix is cut into
 constexpr int kHdrPartSlots = 4;    // partial slots the plan uses (<= part_capacity)
 constexpr int kHdrPrefixPartTokens = 5;  // keys per shared-prefix partition (multiple of 64)
-constexpr int kHdrSize = 6;
-constexpr int kHdrInfo = 6;         // fields reported by pa_attention_plan_info
+constexpr int kHdrPartTokens = 6;   // decode partition length P of this plan
+constexpr int kHdrSize = 7;
+constexpr int kHdrInfo = 7;         // fields reported by pa_attention_plan_info
 
-// Shared-prefix partitions: a partition holds at least prefix_part_min keys, and all
+// Shortest decode partition the planner chooses by itself (a caller may fix a shorter one).
+constexpr int kMinPartTokens = 256;
+
+// Shared-prefix partitions: a partition holds at least min(P, 512) keys, and all
 // decode rows together hold at most max(kPrefixSlotRows, rows) prefix partials per
 // (kv head, column) (one partition each when there are more rows than that): the prefix
 // kernel draws its parallelism from the partitions when there are few rows, and from
@@ -112,12 +117,15 @@ struct WorkspaceLayout {
   size_t total;
 };
 
-// Partition lengths of a step and the partial slots they can need; see choose_partitioning.
+// How a step's decode path is split, as far as the host can know it before the planner
+// runs: the partition length if the caller fixes one, and bounds over every plan of the
+// call's sizes on the tasks and the partial slots; see choose_partitioning.
 struct Partitioning {
-  int32_t part_tokens;      // decode partitions
-  int32_t prefix_part_min;  // shortest shared-prefix partition
-  int32_t max_task_parts;   // decode partitions of the longest sequence the tables allow
-  int64_t part_capacity;    // partial slots: an upper bound on what any plan of these sizes uses
+  int32_t part_tokens;      // fixed partition length, or 0 (chosen by the planner)
+  int32_t decode_slots;     // tasks the planner aims for
+  int32_t max_tasks;        // bound on decode tasks
+  int64_t part_capacity;    // bound on partial slots
+  int32_t num_kv_heads;
 };
 Partitioning choose_partitioning(int32_t num_seqs, int32_t max_blocks, int64_t num_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads);
@@ -193,6 +201,12 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+
+// Integer minimum and maximum of 64-bit values. (In device code, min<int64_t>(...) can
+// resolve to the floating-point overload, which silently turns later integer divisions
+// into exact ones.)
+__host__ __device__ inline int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ inline int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 // Largest i in [0, n) with a[i] <= x, for non-decreasing a[0..n] and a[0] <= x < a[n].
 __device__ inline int upper_index(const int32_t* a, int n, int64_t x) {

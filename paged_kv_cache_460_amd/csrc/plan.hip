@@ -35,89 +35,119 @@ namespace pa {
 namespace {
 constexpr int kBuckets = 32;
 constexpr int kMinPrefixBlocks = 4;  // shorter shared runs are left to the decode kernel
+constexpr int kLdsSeqs = 2048;       // sequences whose lengths the planner stages in LDS
 
-// Block-wide exclusive scan and minimum for the 1024-thread planner: within each wave by
-// cross-lane shuffles, then over the 16 wave results through LDS (two barriers each).
-__device__ inline int block_exclusive_scan(int32_t* wsum, int tid, int value, int& total) {
-  const int lane = tid & 63, w = tid >> 6;
-  int v = value;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int x = wsum[k];
-    before += k < w ? x : 0;
-    all += x;
-  }
-  __syncthreads();  // wsum may be reused by the next call
-  total = all;
-  return before + v - value;
+// Inclusive scans over the lanes of a wave by DPP lane shifts, which run on the VALU
+// with no LDS traffic (cross-lane shuffles through LDS, issued by all 16 waves of the
+// planner at once, kept its LDS pipe busy for microseconds per reduction): within each
+// row of 16 lanes by shifts of 1, 2, 4 and 8, then across rows by broadcasting lane 15
+// into rows 1 and 3 and lane 31 into rows 2 and 3. Lanes without a source add 0 (sum)
+// or keep their own value (minimum).
+__device__ inline int row_scan_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return v;
+}
+__device__ inline int wave_scan_add(int v) {
+  v = row_scan_add(v);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+__device__ inline int row_scan_min(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false));
+  return v;
+}
+__device__ inline int wave_scan_min(int v) {
+  v = row_scan_min(v);
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false));
+  return v;
 }
 
-// The same scan over 64-bit values (partial-slot offsets).
-__device__ inline int64_t block_exclusive_scan64(int64_t* wsum, int tid, int64_t value, int64_t& total) {
-  const int lane = tid & 63, w = tid >> 6;
-  int64_t v = value;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  int64_t before = 0, all = 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int64_t x = wsum[k];
-    before += k < w ? x : 0;
-    all += x;
-  }
-  __syncthreads();
-  total = all;
-  return before + v - value;
+// Workgroup barrier that orders LDS accesses only. The planner never reads back the
+// global stores it makes, so its barriers need not wait for them to complete (a full
+// __syncthreads would).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ inline int block_min(int32_t* wsum, int tid, int value) {
-  const int lane = tid & 63, w = tid >> 6;
-  int v = value;
+// Block-wide reductions for the 1024-thread planner, several 32-bit values at a time:
+// within each wave by DPP scans, then over the 16 wave results (one per lane of the first
+// row, scanned once more); two LDS barriers per call, whatever the number of values.
+// Exclusive scans (and totals) of the first NS values, minimums of the next NM.
+template <int NS, int NM>
+__device__ inline void block_scan_min(int32_t (*red)[8], int tid, const int32_t* sv, int32_t* before, int32_t* total,
+                                      int32_t* mv) {
+  static_assert(NS + NM <= 8, "at most 8 values per call");
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int32_t inc[NS > 0 ? NS : 1];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-  if (lane == 0) wsum[w] = v;
-  __syncthreads();
-  int r = wsum[0];
+  for (int k = 0; k < NS; ++k) inc[k] = wave_scan_add(sv[k]);
 #pragma unroll
-  for (int k = 1; k < 16; ++k) r = min(r, wsum[k]);
-  __syncthreads();
-  return r;
+  for (int k = 0; k < NM; ++k) mv[k] = wave_scan_min(mv[k]);
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) red[w][k] = inc[k];
+#pragma unroll
+    for (int k = 0; k < NM; ++k) red[w][NS + k] = mv[k];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int32_t x = row_scan_add(lane < 16 ? red[lane][k] : 0);  // inclusive over the waves
+    total[k] = __builtin_amdgcn_readlane(x, 15);
+    const int32_t bw = w > 0 ? __builtin_amdgcn_readlane(x, w - 1) : 0;
+    before[k] = bw + inc[k] - sv[k];
+  }
+#pragma unroll
+  for (int k = 0; k < NM; ++k) mv[k] = __builtin_amdgcn_readlane(row_scan_min(lane < 16 ? red[lane][NS + k] : INT32_MAX), 15);
+  lds_barrier();  // red may be reused by the next call
 }
 }  // namespace
 
 // The planner, run by one workgroup of 1024 threads.
 __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
-  __shared__ int32_t sums[16];  // per-wave partial results of the block reductions
-  __shared__ int64_t sums64[16];
+  __shared__ int32_t red[16][8];  // per-wave partial results of the block reductions
   __shared__ int32_t bcount[kBuckets];
   __shared__ int32_t bfill[kBuckets];
   __shared__ int32_t boff[kBuckets];
+  // Query rows, lengths and first block id of each sequence, staged once (steps of up
+  // to kLdsSeqs sequences; larger ones read them from memory each time).
+  __shared__ int32_t s_rows[kLdsSeqs], s_len[kLdsSeqs], s_b0[kLdsSeqs];
   const int32_t* __restrict__ qsl = p.qsl;
   const int32_t* __restrict__ seq_lens = p.seq_lens;
   const int num_seqs = p.num_seqs;
   const int tid = threadIdx.x;
+  const int MB = p.max_blocks;
+  const int hkv = p.num_kv_heads;
+  const bool staged = num_seqs <= kLdsSeqs;
   if (tid < kBuckets) {
     bcount[tid] = 0;
     bfill[tid] = 0;
   }
+  if (staged) {
+    for (int i = tid; i < num_seqs; i += 1024) {
+      s_rows[i] = qsl[i + 1] - qsl[i];
+      s_len[i] = seq_lens[i];
+      s_b0[i] = p.block_tables[(int64_t)i * MB];
+    }
+  }
+  lds_barrier();
+  auto rows_of = [&](int i) { return staged ? s_rows[i] : qsl[i + 1] - qsl[i]; };
+  auto len_of = [&](int i) { return staged ? s_len[i] : seq_lens[i]; };
+  auto b0_of = [&](int i) { return staged ? s_b0[i] : p.block_tables[(int64_t)i * MB]; };
   const int per = (num_seqs + 1023) / 1024;
   const int b = tid * per;
   const int e = min(num_seqs, b + per);
-  const int P = p.part_tokens;
-  const int MB = p.max_blocks;
 
   // A sequence of 2..16/G rows is a short multi-row step (speculative verification):
   // the decode kernel takes it, its (row, head) pairs filling the MFMA columns.
@@ -125,129 +155,158 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
   auto is_multi = [&](int n) { return n >= 2 && n * G <= 16; };
   auto is_chunk = [&](int n) { return n >= 2 && n * G > 16; };
 
-  // ---- prefill tiles, decode sequence list ----
-  int tiles = 0, ndec = 0;
+  // ---- one pass over the sequences: prefill tiles, decode rows, decode-path keys, and
+  // what the shared-prefix test needs (first decode row, shortest cached run, range of
+  // first block ids) ----
+  // Keys are counted in whole 32-key steps (an upper bound on the keys), so that every
+  // sum fits 32 bits.
+  constexpr int32_t kBig = INT32_MAX;
+  int32_t cnt[4] = {0, 0, 0, 0};  // tiles, decode rows, decode-row key steps, multi-row key steps
+  int32_t mins[4] = {kBig, kBig, kBig, kBig};  // first decode row, cached blocks, min b0, -max b0
   for (int i = b; i < e; ++i) {
-    const int n = qsl[i + 1] - qsl[i];
-    if (is_chunk(n)) tiles += (n + rows_per_tile - 1) / rows_per_tile;
-    else if (n == 1) ++ndec;
+    const int n = rows_of(i);
+    if (is_chunk(n)) {
+      cnt[0] += (n + rows_per_tile - 1) / rows_per_tile;
+    } else if (n == 1) {
+      const int L = len_of(i), b0 = b0_of(i);
+      cnt[1] += 1;
+      cnt[2] += (L + 31) / 32;
+      mins[0] = min(mins[0], i);
+      mins[1] = min(mins[1], (L - 1) / kBlock);  // blocks holding only cached tokens
+      mins[2] = min(mins[2], b0);
+      mins[3] = min(mins[3], -b0);
+    } else if (is_multi(n)) {
+      cnt[3] += (len_of(i) + 31) / 32;
+    }
   }
-  int total_tiles, total_dec;
-  int tile_run = block_exclusive_scan(sums, tid, tiles, total_tiles);
-  int dec_run = block_exclusive_scan(sums, tid, ndec, total_dec);
-  for (int i = b; i < e; ++i) {
-    p.tile_offsets[i] = tile_run;
-    const int n = qsl[i + 1] - qsl[i];
-    if (is_chunk(n)) tile_run += (n + rows_per_tile - 1) / rows_per_tile;
-    else if (n == 1) p.dec_seqs[dec_run++] = i;
+  int32_t before[4], total[4];
+  block_scan_min<4, 4>(red, tid, cnt, before, total, mins);
+  const int total_tiles = total[0], total_dec = total[1];
+  {
+    int tile_run = before[0], dec_run = before[1];
+    for (int i = b; i < e; ++i) {
+      p.tile_offsets[i] = tile_run;
+      const int n = rows_of(i);
+      if (is_chunk(n)) tile_run += (n + rows_per_tile - 1) / rows_per_tile;
+      else if (n == 1) p.dec_seqs[dec_run++] = i;
+    }
   }
   if (tid == 0) p.tile_offsets[num_seqs] = total_tiles;
 
   // ---- shared prefix: common leading blocks of every decode sequence ----
-  // The first decode sequence is the reference (found by a block-wide min). Cheap test
-  // first: every decode sequence must hold a cached block 0 equal to the reference's;
-  // only then are all (sequence, block) pairs up to the shortest cached run compared,
-  // in parallel, for the first mismatch.
-  int my_first = 1 << 30;
-  for (int i = b; i < e; ++i)
-    if (qsl[i + 1] - qsl[i] == 1) {
-      my_first = i;
-      break;
-    }
-  const int ref = block_min(sums, tid, my_first);
+  // Cheap test first: every decode row holds at least kMinPrefixBlocks cached blocks and
+  // all start with the same block; only then are all (sequence, block) pairs up to the
+  // shortest cached run compared with the first decode row's, in parallel, for the first
+  // mismatch.
   int prefix_blocks = 0;
-  if (total_dec >= 2) {
-    const int32_t* __restrict__ bref = p.block_tables + (int64_t)ref * MB;
-    int cap_local = 1 << 30, same_first = 1;
-    for (int i = b; i < e; ++i) {
-      if (qsl[i + 1] - qsl[i] != 1) continue;
-      const int cap = (seq_lens[i] - 1) / kBlock;  // blocks holding only cached tokens
-      cap_local = min(cap_local, cap);
-      if (cap == 0 || p.block_tables[(int64_t)i * MB] != bref[0]) same_first = 0;
-    }
-    const int cap = block_min(sums, tid, cap_local);
-    const int all_same_first = block_min(sums, tid, same_first);
-    if (all_same_first && cap >= kMinPrefixBlocks) {
-      // Wave w compares sequences w, w + 16, ... four at a time, its lanes over the
-      // blocks; each lane keeps the first mismatching block it saw. The comparisons are
-      // selects, not branches, so all loads of a round are in flight together.
-      const int lane = tid & 63, w = tid >> 6;
-      int bad = cap;
-      for (int i0 = w; i0 < num_seqs; i0 += 4 * 16) {
-        bool dec[4];
-        const int32_t* __restrict__ row[4];
+  const int cap = mins[1];
+  if (total_dec >= 2 && mins[2] == -mins[3] && cap >= kMinPrefixBlocks) {
+    const int32_t* __restrict__ bref = p.block_tables + mins[0] * MB;
+    // Wave w compares sequences w, w + 16, ... four at a time, its lanes over the
+    // blocks; each lane keeps the first mismatching block it saw. The comparisons are
+    // selects, not branches, so all loads of a round are in flight together.
+    const int lane = tid & 63, w = tid >> 6;
+    int bad = cap;
+    for (int i0 = w; i0 < num_seqs; i0 += 4 * 16) {
+      bool dec[4];
+      const int32_t* __restrict__ row[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + 16 * u;
-          dec[u] = i < num_seqs && qsl[i + 1] - qsl[i] == 1;
-          row[u] = p.block_tables + (int64_t)min(i, num_seqs - 1) * MB;
-        }
-        for (int c = lane; c < cap; c += 64) {
-          const int r = bref[c];
-          int x[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) x[u] = row[u][c];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) bad = (dec[u] && x[u] != r) ? min(bad, c) : bad;
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(i0 + 16 * u, num_seqs - 1);
+        dec[u] = i0 + 16 * u < num_seqs && rows_of(i) == 1;
+        row[u] = p.block_tables + (int64_t)i * MB;
       }
-      prefix_blocks = block_min(sums, tid, bad);
+      for (int c = lane; c < cap; c += 64) {
+        const int r = bref[c];
+        int x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = row[u][c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bad = (dec[u] && x[u] != r) ? min(bad, c) : bad;
+      }
     }
+    int32_t m[1] = {bad};
+    block_scan_min<0, 1>(red, tid, nullptr, nullptr, nullptr, m);
+    prefix_blocks = m[0];
   }
   if (prefix_blocks < kMinPrefixBlocks) prefix_blocks = 0;
-  int prefix_keys = prefix_blocks * kBlock;
-  // Shared-prefix partitions: at least prefix_part_min keys each (a multiple of 64), and
-  // at most max(kPrefixSlotRows / decode rows, 1) of them, which bounds the partials.
+  const int prefix_keys = prefix_blocks * kBlock;
+
+  // ---- decode-path tasks: partitions of each decode suffix [prefix_keys, L) and of each
+  // multi-row sequence's whole range [0, L) ----
+  auto task_len = [&](int i) {
+    const int n = rows_of(i);
+    return n == 1 ? len_of(i) - prefix_keys : (is_multi(n) ? len_of(i) : 0);
+  };
+  // Partition length P: the caller's, or chosen here from the step's actual lengths so
+  // that the decode-path keys fill about decode_slots (kv head, partition) tasks of equal
+  // length: P = keys * Hkv / slots in whole 32-key steps, at least kMinPartTokens, then
+  // raised in proportion if the whole-partition rounding of each sequence overshoots the
+  // slots. A sequence shorter than P stays whole.
+  int P = p.part_tokens;
+  if (P == 0) {
+    const int64_t keys = 32 * ((int64_t)total[2] + total[3]) - (int64_t)total_dec * prefix_keys;
+    const int64_t slots = p.decode_slots;
+    int64_t want = (keys * hkv + slots - 1) / slots;
+    want = imin64(imax64((want + 31) / 32 * 32, kMinPartTokens), 1 << 30);
+    int32_t nt[1] = {0};
+    for (int i = b; i < e; ++i) nt[0] += split_parts(task_len(i), (int)want).n;
+    int32_t nb[1], ntot[1];
+    block_scan_min<1, 0>(red, tid, nt, nb, ntot, nullptr);
+    if ((int64_t)ntot[0] * hkv > slots)
+      want = imin64((want * ntot[0] * hkv + slots - 1) / slots + 31, 1 << 30) / 32 * 32;
+    P = (int)want;
+  }
+  // Shared-prefix partitions: at least min(P, 512) keys each (a multiple of 64), and at
+  // most max(kPrefixSlotRows / decode rows, 1) of them, which bounds the partials.
   int pparts = 0, pplen = 0;
   if (prefix_keys > 0) {
-    const int pmin = p.prefix_part_min;
+    const int pmin = (min(P, 512) + 63) / 64 * 64;
     int n = (prefix_keys + pmin - 1) / pmin;
     n = min(n, max(1, kPrefixSlotRows / total_dec));
     pplen = ((prefix_keys + n - 1) / n + 63) / 64 * 64;
     pparts = (prefix_keys + pplen - 1) / pplen;
   }
-
-  // ---- decode-path tasks: partitions of each decode suffix [prefix_keys, L) and of each
-  // multi-row sequence's whole range [0, L) ----
-  auto task_len = [&](int i) {
-    const int n = qsl[i + 1] - qsl[i];
-    return n == 1 ? seq_lens[i] - prefix_keys : (is_multi(n) ? seq_lens[i] : 0);
-  };
-  // Partial slots of sequence i: nparts * Hkv * live columns when its result is split
-  // over two or more partitions (shared-prefix ones included), else none.
-  const int hkv = p.num_kv_heads;
-  auto part_slots = [&](int i) -> int64_t {
-    const int n = qsl[i + 1] - qsl[i];
+  // Partials of sequence i, in units of Hkv * G slots: nparts * rows (its live columns
+  // are rows * G) when its result is split over two or more partitions (shared-prefix
+  // ones included), else none.
+  auto part_units = [&](int i) -> int {
+    const int n = rows_of(i);
     if (n != 1 && !is_multi(n)) return 0;
     const int nparts = (n == 1 ? pparts : 0) + split_parts(task_len(i), P).n;
-    return nparts >= 2 ? (int64_t)nparts * hkv * n * G : 0;
+    return nparts >= 2 ? nparts * n : 0;
   };
+  const int64_t unit_slots = (int64_t)hkv * G;
   // Tasks of exactly P keys come first, in sequence order; the others follow in 32 length
-  // buckets, longest bucket first.
-  auto bucket = [&](int tlen) { return (tlen - 1) * kBuckets / P; };
-  auto tlen_of = [&](const PartSplit& sp, int len, int q) { return q + 1 < sp.n ? sp.plen : len - (sp.n - 1) * sp.plen; };
-  int full = 0;
-  int64_t my_slots = 0;
+  // buckets over (0, min(P, longest table)], longest bucket first.
+  const int Pb = (int)imin64(P, (int64_t)MB * kBlock);
+  auto bucket = [&](int tlen) { return min(kBuckets - 1, (tlen - 1) * kBuckets / Pb); };
+  // A sequence's partitions all hold plen keys but the last, so its tasks fall in at
+  // most two buckets: one LDS atomic each, for all of them.
+  int32_t tc[3] = {0, 0, 0};  // tasks of exactly P keys, all tasks, partial units
   for (int i = b; i < e; ++i) {
     const int len = task_len(i);
     const PartSplit sp = split_parts(len, P);
-    for (int q = 0; q < sp.n; ++q) {
-      const int t = tlen_of(sp, len, q);
-      if (t == P) ++full;
-      else atomicAdd(&bcount[bucket(t)], 1);
+    if (sp.n == 0) continue;
+    tc[1] += sp.n;
+    const int last = len - (sp.n - 1) * sp.plen;
+    if (sp.n > 1) {
+      if (sp.plen == P) tc[0] += sp.n - 1;
+      else atomicAdd(&bcount[bucket(sp.plen)], sp.n - 1);
     }
-    my_slots += part_slots(i);
+    if (last == P) ++tc[0];
+    else atomicAdd(&bcount[bucket(last)], 1);
+    tc[2] += part_units(i);
   }
-  int total_full;
-  int full_run = block_exclusive_scan(sums, tid, full, total_full);
-  int64_t total_slots;
-  int64_t slot_run = block_exclusive_scan64(sums64, tid, my_slots, total_slots);
-  // The host sizes the partial area from an upper bound over every plan of these sizes,
-  // so this cannot overflow; if it ever did, nothing on the decode path runs (its rows
-  // stay unwritten) rather than writing past the workspace.
-  const bool overflow = total_slots > p.part_capacity;
+  int32_t tb[3], tt[3];
+  block_scan_min<3, 0>(red, tid, tc, tb, tt, nullptr);  // (its barriers also publish bcount)
+  // The host sizes the task list, the decode grid and the partial area from upper bounds
+  // over every plan of these sizes, so this cannot overflow; if it ever did, nothing on
+  // the decode path runs (its rows stay unwritten) rather than writing past the workspace.
+  const int64_t total_slots = tt[2] * unit_slots;
+  const bool overflow = total_slots > p.part_capacity || tt[1] > p.max_tasks;
   if (tid == 0) {
-    int run = total_full;
+    int run = tt[0];
     for (int k = kBuckets - 1; k >= 0; --k) {
       boff[k] = run;
       run += bcount[k];
@@ -256,21 +315,40 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
     p.plan_hdr[kHdrDecSeqs] = total_dec;
     p.plan_hdr[kHdrPrefixKeys] = overflow ? 0 : prefix_keys;
     p.plan_hdr[kHdrPrefixParts] = overflow ? 0 : pparts;
-    p.plan_hdr[kHdrPartSlots] = overflow ? -1 : (int)min(total_slots, (int64_t)INT32_MAX);
+    p.plan_hdr[kHdrPartSlots] = overflow ? -1 : (int)imin64(total_slots, INT32_MAX);
     p.plan_hdr[kHdrPrefixPartTokens] = pplen;
+    p.plan_hdr[kHdrPartTokens] = P;
   }
-  __syncthreads();
+  lds_barrier();
+  if (overflow) return;
+  int full_run = tb[0];
+  int64_t unit_run = tb[2];
   for (int i = b; i < e; ++i) {
     const int len = task_len(i);
     const PartSplit sp = split_parts(len, P);
-    for (int q = 0; q < sp.n; ++q) {
-      const int t = tlen_of(sp, len, q);
-      const int slot = t == P ? full_run++ : boff[bucket(t)] + atomicAdd(&bfill[bucket(t)], 1);
-      p.dec_tasks[2 * slot] = i;
-      p.dec_tasks[2 * slot + 1] = q;
+    if (sp.n > 0) {
+      const int last = len - (sp.n - 1) * sp.plen;
+      if (sp.n > 1) {
+        int at;
+        if (sp.plen == P) {
+          at = full_run;
+          full_run += sp.n - 1;
+        } else {
+          const int bk = bucket(sp.plen);
+          at = boff[bk] + atomicAdd(&bfill[bk], sp.n - 1);
+        }
+        for (int q = 0; q + 1 < sp.n; ++q) {
+          p.dec_tasks[2 * (at + q)] = i;
+          p.dec_tasks[2 * (at + q) + 1] = q;
+        }
+      }
+      const int bk = bucket(last);
+      const int at = last == P ? full_run++ : boff[bk] + atomicAdd(&bfill[bk], 1);
+      p.dec_tasks[2 * at] = i;
+      p.dec_tasks[2 * at + 1] = sp.n - 1;
     }
-    p.part_base[i] = slot_run;
-    slot_run += part_slots(i);
+    p.part_base[i] = unit_run * unit_slots;
+    unit_run += part_units(i);
   }
 }
 

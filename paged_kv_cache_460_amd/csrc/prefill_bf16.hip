@@ -446,7 +446,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       // partial of shared-prefix partition seq_or_pp for decode sequence dec_seqs[crow]:
       // unnormalised o, running max and weight sum (the merge kernel finishes the row)
       const int i = p.dec_seqs[crow[s]];
-      const int nparts = p.plan_hdr[kHdrPrefixParts] + split_parts(p.seq_lens[i] - L, p.part_tokens).n;
+      const int nparts = p.plan_hdr[kHdrPrefixParts] + split_parts(p.seq_lens[i] - L, p.plan_hdr[kHdrPartTokens]).n;
       const int64_t slot = part_slot(p.part_base[i], nparts, G, g, col % G, seq_or_pp);
       float* po = p.part_o + slot * D + 4 * h2;
 #pragma unroll
@@ -513,8 +513,10 @@ hipError_t launch_prefix_bf16(const AttnParams& p, hipStream_t stream) {
   // Workgroups past the planned tasks exit at once.
   const int64_t R = prefill_rows_per_tile(p.group);
   const int64_t max_len = (int64_t)p.max_blocks * kBlock;
-  const int64_t pparts = std::min<int64_t>((max_len + p.prefix_part_min - 1) / p.prefix_part_min,
-                                           kPrefixSlotRows / 2);
+  // shortest prefix partition: min(P, 512) in whole 64-key tiles, P >= kMinPartTokens
+  // unless the caller fixed it
+  const int64_t pmin = (std::min(p.part_tokens ? p.part_tokens : kMinPartTokens, 512) + 63) / 64 * 64;
+  const int64_t pparts = std::min<int64_t>((max_len + pmin - 1) / pmin, kPrefixSlotRows / 2);
   const int64_t rows = std::min<int64_t>(p.num_seqs, p.num_tokens);
   const int64_t tiles = (std::max<int64_t>(kPrefixSlotRows, rows) + pparts * (R - 1) + R - 1) / R;
   const int64_t grid = tiles * p.num_kv_heads;

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnParams p) {
   const int ncols = nrows * G;
   if (nrows < 1 || ncols > 16 || wave * kCpw >= ncols) return;  // off the decode path, or idle
   if (p.plan_hdr[kHdrPartSlots] < 0) return;  // no plan (see the planner)
-  const int P = p.part_tokens;
+  const int P = p.plan_hdr[kHdrPartTokens];
   const int prefix_keys = nrows == 1 ? p.plan_hdr[kHdrPrefixKeys] : 0;
   const int prefix_parts = nrows == 1 ? p.plan_hdr[kHdrPrefixParts] : 0;
   const int nparts = prefix_parts + split_parts(p.seq_lens[i] - prefix_keys, P).n;

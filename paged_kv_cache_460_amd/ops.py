@@ -195,11 +195,12 @@ def attention_plan_info(workspace, q, k_cache, block_tables):
     T, hq, d = q.shape
     hkv = k_cache.shape[1]
     S, MB = block_tables.shape
-    info = (ctypes.c_int32 * 6)()
+    info = (ctypes.c_int32 * 7)()
     _check(lib.pa_attention_plan_info(_ptr(workspace), workspace.numel(), S, MB, T, hq, hkv, d,
                                       _payload_dtype(q, "q"), info, _stream(q)))
     return {"decode_tasks": info[0], "decode_rows": info[1], "shared_prefix_keys": info[2],
-            "shared_prefix_parts": info[3], "partial_slots": info[4], "shared_prefix_part_keys": info[5]}
+            "shared_prefix_parts": info[3], "partial_slots": info[4], "shared_prefix_part_keys": info[5],
+            "partition_tokens": info[6]}
 
 
 def step(q, k, v, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out=None,
