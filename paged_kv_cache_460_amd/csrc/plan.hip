@@ -203,8 +203,10 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
   if (total_dec >= 2 && mins[2] == -mins[3] && cap >= kMinPrefixBlocks) {
     const int32_t* __restrict__ bref = p.block_tables + mins[0] * MB;
     // Wave w compares sequences w, w + 16, ... four at a time, its lanes over the
-    // blocks; each lane keeps the first mismatching block it saw. The comparisons are
-    // selects, not branches, so all loads of a round are in flight together.
+    // blocks, four blocks per lane at a time; each lane keeps the first mismatching block
+    // it saw. The comparisons are selects, not branches, so all 20 loads of a round are
+    // in flight together. (Indices past the run are clamped to its last block: every
+    // table row holds MB >= cap entries.)
     const int lane = tid & 63, w = tid >> 6;
     int bad = cap;
     for (int i0 = w; i0 < num_seqs; i0 += 4 * 16) {
@@ -216,13 +218,19 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
         dec[u] = i0 + 16 * u < num_seqs && rows_of(i) == 1;
         row[u] = p.block_tables + (int64_t)i * MB;
       }
-      for (int c = lane; c < cap; c += 64) {
-        const int r = bref[c];
-        int x[4];
+      for (int c0 = lane; c0 < cap; c0 += 4 * 64) {
+        int r[4], x[4][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = row[u][c];
+        for (int v = 0; v < 4; ++v) {
+          const int cc = min(c0 + 64 * v, cap - 1);
+          r[v] = bref[cc];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) bad = (dec[u] && x[u] != r) ? min(bad, c) : bad;
+          for (int u = 0; u < 4; ++u) x[u][v] = row[u][cc];
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) bad = (dec[u] && x[u][v] != r[v]) ? min(bad, c0 + 64 * v) : bad;
       }
     }
     int32_t m[1] = {bad};

@@ -319,14 +319,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       any_raise |= raise;
       mnew[s] = raise ? mxs : m[s];
       const float nm = -mnew[s];
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      float ps[4];
 #pragma unroll
       for (int ub = 0; ub < 4; ++ub) {
         float pe[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][ub >> 1][(ub & 1) * 8 + e], sl2, nm));
-          ps[e & 3] += pe[e];
+          ps[e & 3] = (ub == 0 && e < 4) ? pe[e] : ps[e & 3] + pe[e];  // no + 0 to start
         }
         const u32x4 w = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
                          pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
