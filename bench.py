@@ -160,7 +160,8 @@ def cpu_baseline(step, frac):
         "cpu_model": cpu_model,
         "blas": blas,
         "kind": "oracle",
-        "sample": f"every {stride}th row of the step ({len(rows)} of {T} rows, {len(seqs)} sequences), "
+        "sample": (f"every {stride}th row of the step" if stride > 1 else "every row of the step") +
+                  f" ({len(rows)} of {T} rows, {len(seqs)} sequences), "
                   f"fp64 numpy; slot mapping, cache write and attention for those rows; {secs:.1f} s",
         "seconds": secs,
     }
@@ -342,7 +343,10 @@ def main():
             "prefill_tflops": tflops(work["prefill_flops"], ms["prefill"]),
             "prefix_tflops": tflops(work["prefix_flops"], ms["prefix"]),
         }
-        for k in ("decode_kv_gbps", "decode_kv_unique_gbps", "decode_kernel_gbps"):
+        # Fractions of HBM peak only for bytes that reach HBM: each physical block once
+        # (unique), and what the decode kernel itself reads. The logical rate counts a
+        # shared prefix once per sequence, so it can exceed HBM peak and gets no fraction.
+        for k in ("decode_kv_unique_gbps", "decode_kernel_gbps"):
             r[k.replace("gbps", "hbm_frac")] = r[k] / HBM_PEAK_GBPS if r[k] else None
         for k in ("prefill", "prefix"):
             t = r[f"{k}_tflops"]
@@ -409,7 +413,7 @@ def main():
             "prefix_flops_per_launch": work["prefix_flops"],
             "scatter_bytes_per_launch": work["scatter_bytes"],
             "decode_kv_gbps": warm["decode_kv_gbps"],
-            "decode_hbm_frac": warm["decode_kv_hbm_frac"],
+            "decode_hbm_frac": warm["decode_kv_unique_hbm_frac"],
             "prefill_mfma_util": warm["prefill_mfma_util"],
             "execution": mode,
             "ms_per_step_median": step_median,

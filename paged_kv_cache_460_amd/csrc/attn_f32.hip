@@ -2,9 +2,11 @@
 //
 // fp32 payloads need fp32 products (the bf16 matrix cores would round the inputs), so
 // this path keeps everything on the VALU: one wave per (query row, kv head) walks the
-// row's visible keys 64 at a time (one key per lane for the dot products, then one
-// dimension slice per lane for the value sum), with an online softmax per query head.
-// It is the straightforward path for fp32 steps; bf16 steps use the MFMA kernels.
+// row's visible keys 64 at a time, with an online softmax per query head. For the dot
+// products a lane holds one key, its row read once in 16-byte pieces and used for every
+// query head of the group; for the value sum a lane holds one dimension (two for D =
+// 128), reading that dimension's 16 tokens of a block (64 contiguous bytes of the
+// dim-major value tile) at a time. bf16 steps use the MFMA kernels.
 #include "pa_internal.h"
 
 namespace pa {
@@ -60,6 +62,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
   }
 
   for (int kb = 0; kb <= pos; kb += 64) {
+    // Scores: lane = key kb + lane. Its key row is read once, 16 bytes at a time, and
+    // dotted with every query head of the group (queries from LDS, broadcast reads).
     const int j = kb + lane;
     const bool valid = j <= pos;
     float s[kMaxG];
@@ -67,12 +71,23 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
     for (int h = 0; h < kMaxG; ++h) s[h] = -INFINITY;
     if (valid) {
       const int64_t blk = bt[j / kBlock];
-      const float* kr = kc + ((blk * hkv + g) * kBlock + j % kBlock) * D;
+      const f32x4* kr = reinterpret_cast<const f32x4*>(kc + ((blk * hkv + g) * kBlock + j % kBlock) * D);
+      f32x4 kv[D / 4];
+#pragma unroll
+      for (int d4 = 0; d4 < D / 4; ++d4) kv[d4] = kr[d4];
 #pragma unroll
       for (int h = 0; h < kMaxG; ++h) {
         if (h < G) {
+          const f32x4* qh = reinterpret_cast<const f32x4*>(qs + h * D);
           float acc = 0.f;
-          for (int d = 0; d < D; ++d) acc = fmaf(qs[h * D + d], kr[d], acc);
+#pragma unroll
+          for (int d4 = 0; d4 < D / 4; ++d4) {
+            const f32x4 qv = qh[d4];
+            acc = fmaf(qv[0], kv[d4][0], acc);
+            acc = fmaf(qv[1], kv[d4][1], acc);
+            acc = fmaf(qv[2], kv[d4][2], acc);
+            acc = fmaf(qv[3], kv[d4][3], acc);
+          }
           s[h] = acc * sl2;
         }
       }
@@ -91,17 +106,26 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
       }
     }
     __syncthreads();
+    // Values: lane = dimension (and + 64). Per 16-key block, a dimension's 16 tokens are
+    // 64 contiguous bytes of the dim-major value tile, read as four 16-byte pieces; keys
+    // past the row's position are removed by select (their slots may hold NaN).
     const int nk = min(64, pos + 1 - kb);
-    for (int jj = 0; jj < nk; ++jj) {
-      const int key = kb + jj;
-      const int64_t blk = bt[key / kBlock];
-      const float* vr = vc + (blk * hkv + g) * D * kBlock + key % kBlock;
+    for (int b0 = 0; b0 < nk; b0 += kBlock) {
+      const int64_t blk = bt[(kb + b0) / kBlock];
+      const int nv = min(kBlock, nk - b0);
 #pragma unroll
       for (int x = 0; x < kPer; ++x) {
-        const float vv = vr[(int64_t)(lane + 64 * x) * kBlock];
+        const f32x4* vr = reinterpret_cast<const f32x4*>(vc + ((blk * hkv + g) * D + lane + 64 * x) * kBlock);
+        f32x4 vv[4];
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h)
-          if (h < G) o[h][x] = fmaf(ps[h * 64 + jj], vv, o[h][x]);
+        for (int c = 0; c < 4; ++c) vv[c] = vr[c];
+#pragma unroll
+        for (int kk = 0; kk < kBlock; ++kk) {
+          const float v = kk < nv ? vv[kk >> 2][kk & 3] : 0.f;
+#pragma unroll
+          for (int h = 0; h < kMaxG; ++h)
+            if (h < G) o[h][x] = fmaf(ps[h * 64 + b0 + kk], v, o[h][x]);
+        }
       }
     }
     __syncthreads();
