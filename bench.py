@@ -16,10 +16,11 @@ timed region starts.
 Prints one JSON line with the whole-step rate (tokens/s) and, from per-kernel HIP-event
 durations of eager steps: the dominant kernel's roofline (decode: KV bytes it reads per
 launch / its duration, against HBM peak; prefill: causal flops / duration, against bf16
-MFMA peak); the decode side's KV rate over t_dec = plan + shared-prefix + decode + merge
-time, logical (every decode-path sequence's tokens) and unique (each physical block
-once), warm (steps back to back) and cold (1 GiB read before each step); and the CPU
-oracle's rate on a bounded sample of the same step.
+MFMA peak; the fp32 kernel: flops / duration, against the fp32 vector peak); the decode
+side's KV rate over t_dec = plan + shared-prefix + decode + merge time, logical (every
+decode-path sequence's tokens) and unique (each physical block once), warm (steps back to
+back) and cold (1 GiB read before each step); and the CPU oracle's rate on a bounded
+sample of the same step.
 """
 
 from __future__ import annotations
@@ -38,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged-attn decode KV GB/s (% HBM peak); mixed-step tokens/s; prefill MFMA util"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (256 CUs x 2.4 GHz x 256 flop/clk), TFLOP/s
 
 
 def log(msg):
@@ -77,12 +79,16 @@ def step_work(step, prefix_keys=0):
     pairs = int((qlen[ch] * ctx[ch] + qlen[ch] * (qlen[ch] + 1) // 2).sum())
     prefill_flops = 4 * d * hq * pairs
     prefix_flops = 4 * d * hq * int(single.sum()) * prefix_keys if prefix_keys else 0
+    # fp32 steps: one kernel attends every row to its causal range
+    all_pairs = int((qlen * ctx + qlen * (qlen + 1) // 2).sum())
+    f32_flops = 4 * d * hq * all_pairs if step.dtype == "f32" else 0
     scatter_bytes = int(qlen.sum()) * tok_bytes * 2  # read + write, K and V
     return {"decode_kv_bytes": logical, "decode_kv_unique_bytes": unique, "decode_kernel_kv_bytes": decode_kernel,
             "decode_rows": int(single.sum()), "decode_path_seqs": int(dec.sum()), "chunk_seqs": int(ch.sum()),
             "prefill_flops": prefill_flops, "prefill_causal_pairs_per_head": pairs,
             "prefix_keys": int(prefix_keys), "prefix_flops": prefix_flops,
-            "prefix_kv_bytes": int(prefix_keys) * tok_bytes, "scatter_bytes": scatter_bytes}
+            "prefix_kv_bytes": int(prefix_keys) * tok_bytes, "scatter_bytes": scatter_bytes,
+            "attn_f32_flops": f32_flops}
 
 
 def profiled_traffic(workload_name):
@@ -160,7 +166,7 @@ def cpu_baseline(step, frac):
         "cpu_model": cpu_model,
         "blas": blas,
         "kind": "oracle",
-        "sample": (f"every {stride}th row of the step" if stride > 1 else "every row of the step") +
+        "sample": (f"one row in {stride} of the step" if stride > 1 else "every row of the step") +
                   f" ({len(rows)} of {T} rows, {len(seqs)} sequences), "
                   f"fp64 numpy; slot mapping, cache write and attention for those rows; {secs:.1f} s",
         "seconds": secs,
@@ -342,6 +348,7 @@ def main():
             "decode_kernel_gbps": gbps(work["decode_kernel_kv_bytes"], ms["decode"]),
             "prefill_tflops": tflops(work["prefill_flops"], ms["prefill"]),
             "prefix_tflops": tflops(work["prefix_flops"], ms["prefix"]),
+            "attn_f32_tflops": tflops(work["attn_f32_flops"], ms["attn_f32"]),
         }
         # Fractions of HBM peak only for bytes that reach HBM: each physical block once
         # (unique), and what the decode kernel itself reads. The logical rate counts a
@@ -366,7 +373,8 @@ def main():
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "algorithmic_flops_per_launch": work[f"{dominant}_flops"]}
     else:
-        roof = {"bound": "alu", "kernel": dominant, "achieved": None, "peak": None, "unit": None}
+        roof = {"bound": "alu", "kernel": dominant, "achieved": warm["attn_f32_tflops"], "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "algorithmic_flops_per_launch": work["attn_f32_flops"]}
     roof["frac"] = roof["achieved"] / roof["peak"] if roof["achieved"] and roof["peak"] else None
     roof["traffic"] = profiled_traffic(args.workload) if dominant == "decode" else None
     roof["avg_launch_ms"] = avg_ms[dominant]

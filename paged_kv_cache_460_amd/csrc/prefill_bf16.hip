@@ -170,6 +170,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // srow0: first row (chunk) or first decode-sequence index (prefix) of the strip;
   // crow: this column's row / decode-sequence index; cpos: last key the column sees.
   int srow0[NS], skmax[NS], cpos[NS], crow[NS], qrow[NS];
+  // prefix mode: the column's partial slot, looked up before the tile loop so that the
+  // dependent loads behind it (decode row, its length, its partial base) overlap the tiles
+  int64_t pslot[NS];
   bool cvalid[NS];
   bf16x8 qf[NS][D / 16];
   const int head = g * G + (col % G);
@@ -181,7 +184,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       cvalid[s] = (col < RW * G) && (crow[s] < nds);
       skmax[s] = srow0[s] < nds ? kmax : 0;
       cpos[s] = L - 1;
-      qrow[s] = p.qsl[p.dec_seqs[cvalid[s] ? crow[s] : 0]];
+      const int i = p.dec_seqs[cvalid[s] ? crow[s] : 0];
+      qrow[s] = p.qsl[i];
+      const int nparts = p.plan_hdr[kHdrPrefixParts] + split_parts(p.seq_lens[i] - L, p.plan_hdr[kHdrPartTokens]).n;
+      pslot[s] = part_slot(p.part_base[i], nparts, G, g, col % G, seq_or_pp);
     } else {
       srow0[s] = r0 + (wave * NS + s) * RW;
       const int srows = max(0, min(RW, n - srow0[s]));
@@ -445,9 +451,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if constexpr (kPrefix) {
       // partial of shared-prefix partition seq_or_pp for decode sequence dec_seqs[crow]:
       // unnormalised o, running max and weight sum (the merge kernel finishes the row)
-      const int i = p.dec_seqs[crow[s]];
-      const int nparts = p.plan_hdr[kHdrPrefixParts] + split_parts(p.seq_lens[i] - L, p.plan_hdr[kHdrPartTokens]).n;
-      const int64_t slot = part_slot(p.part_base[i], nparts, G, g, col % G, seq_or_pp);
+      const int64_t slot = pslot[s];
       float* po = p.part_o + slot * D + 4 * h2;
 #pragma unroll
       for (int md = 0; md < D / 32; ++md)

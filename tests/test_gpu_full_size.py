@@ -150,6 +150,34 @@ def test_full_decode_batch():
     assert n == rows_of(step) == 64
 
 
+def test_full_decode_batch_wide_tables():
+    """The decode batch with tables 8192 blocks wide (room for 128K tokens, the extra
+    entries -1): the planner sizes its partitions from the lengths, not the width, so the
+    plan and every output bit equal those of the 256-wide tables."""
+    import paged_kv_cache_460_amd as pa
+
+    res = full_run("decode_batch_bf16")
+    step = res["step"]
+    wide = torch.full((step.num_seqs, 8192), -1, dtype=torch.int32, device=DEV)
+    wide[:, :step.max_blocks_per_seq] = step.block_tables
+
+    def run(tables):
+        ws = torch.empty(pa.attention_workspace_size(step.num_seqs, tables.shape[1], step.num_tokens,
+                                                     step.num_q_heads, step.num_kv_heads, step.head_dim,
+                                                     torch.bfloat16), dtype=torch.uint8, device=DEV)
+        out = torch.full_like(step.q, float("nan"))
+        pa.attention(step.q, res["k_cache"], res["v_cache"], tables, step.seq_lens, step.query_start_loc,
+                     step.context_lens, step.scale, out=out, workspace=ws)
+        return out, ws.numel(), pa.attention_plan_info(ws, step.q, res["k_cache"], tables)
+
+    out_n, ws_n, info_n = run(step.block_tables)
+    out_w, ws_w, info_w = run(wide)
+    log(f"[full] decode batch plan {info_n}, workspace {ws_n >> 20} MiB; 8192-wide tables {ws_w >> 20} MiB")
+    assert info_w == info_n, (info_w, info_n)
+    assert torch.equal(_bits(out_w), _bits(out_n)), "wide tables change the output"
+    assert torch.equal(_bits(out_n), _bits(res["out"])), "workspace call differs from the first"
+
+
 def test_full_prefix_shared():
     import paged_kv_cache_460_amd as pa
 
