@@ -88,27 +88,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int64_t wg = blockIdx.x;
   const int g = (int)(wg % hkv);
   const int64_t t = wg / hkv;
-  if (t >= p.plan_hdr[kHdrDecTasks]) return;
-  const int i = p.dec_tasks[2 * t];
-  const int part = p.dec_tasks[2 * t + 1];
-  const int row = p.qsl[i];
-  const int L = p.seq_lens[i];
-  const int P = p.plan_hdr[kHdrPartTokens];
-  const int G = p.group;
-  const int hq = p.num_q_heads;
   // A task is one KV partition of a decode row or of a short multi-row sequence
   // (speculative-decoding verification: 2..16/G rows), whose (row, head) pairs fill the
-  // MFMA columns. With a shared prefix a decode row covers only the suffix
-  // [prefix_keys, L); the prefix partials occupy its first prefix_parts slots.
-  const int nrows = p.qsl[i + 1] - row;
-  const bool multi = nrows > 1;
-  const int prefix_keys = multi ? 0 : p.plan_hdr[kHdrPrefixKeys];
-  const int prefix_parts = multi ? 0 : p.plan_hdr[kHdrPrefixParts];
-  const PartSplit sp = split_parts(L - prefix_keys, P);
-  const int kbeg = prefix_keys + part * sp.plen;
-  const int kend = min(L, kbeg + sp.plen);
-  const int nparts = prefix_parts + sp.n;
-  const int slot_part = prefix_parts + part;
+  // MFMA columns. With a shared prefix a decode row covers only its suffix; the prefix
+  // partials occupy its first partial slots. The record is read before the task count
+  // is checked (every slot up to the grid's bound is in the list's memory), so that the
+  // two loads overlap.
+  const DecTask task = p.dec_tasks[t];
+  if (t >= p.plan_hdr[kHdrDecTasks]) return;
+  const int i = task.seq;
+  const int row = task.row;
+  const int L = task.len;
+  const int G = p.group;
+  const int hq = p.num_q_heads;
+  const int nrows = task.nrows;
+  const int kbeg = task.kbeg;
+  const int kend = task.kend;
+  const int nparts = task.nparts;
+  const int slot_part = task.slot_part;
+  // the sequence's partial base, loaded now rather than behind the loop (the planner
+  // writes it for every sequence)
+  const int64_t pbase = p.part_base[i];
   // column c = (row r, head-in-group hh); row r sits at position L - nrows + r and sees
   // keys up to it (causal), so its keys stop at climit
   const int cr = c / G, chh = c % G;
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       *reinterpret_cast<u32x2*>(orow + dt * 16) = w;
     }
   } else {
-    const int64_t slot = part_slot(p.part_base[i], nparts, nrows * G, g, c, slot_part);
+    const int64_t slot = part_slot(pbase, nparts, nrows * G, g, c, slot_part);
     float* po = p.part_o + slot * D + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt];

@@ -238,7 +238,7 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t head_dim, pa_dtype dt
   w.plan_hdr = off;
   off += align256(sizeof(int32_t) * kHdrSize);
   w.dec_tasks = off;
-  off += align256(2 * sizeof(int32_t) * (size_t)part.max_tasks);
+  off += align256(sizeof(DecTask) * (size_t)part.max_tasks);
   w.dec_seqs = off;
   off += align256(sizeof(int32_t) * (size_t)num_seqs);
   w.part_base = off;
@@ -461,7 +461,7 @@ pa_status pa_attention(const void* q, const void* k_cache, const void* v_cache, 
   char* base = static_cast<char*>(workspace);
   p.tile_offsets = reinterpret_cast<int32_t*>(base + w.tile_offsets);
   p.plan_hdr = reinterpret_cast<int32_t*>(base + w.plan_hdr);
-  p.dec_tasks = reinterpret_cast<int32_t*>(base + w.dec_tasks);
+  p.dec_tasks = reinterpret_cast<pa::DecTask*>(base + w.dec_tasks);
   p.dec_seqs = reinterpret_cast<int32_t*>(base + w.dec_seqs);
   p.part_base = reinterpret_cast<int64_t*>(base + w.part_base);
   p.part_o = reinterpret_cast<float*>(base + w.part_o);

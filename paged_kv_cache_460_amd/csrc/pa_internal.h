@@ -52,11 +52,26 @@ struct AttnParams {
   float* part_ml;        // [part_capacity, 2] running max (log2 domain) and sum
   // work lists written by the planner
   int32_t* tile_offsets; // [S + 1] exclusive prefix of prefill tiles per sequence
-  int32_t* dec_tasks;    // [max_tasks][2] decode tasks: (sequence, partition)
+  struct DecTask* dec_tasks;  // [max_tasks] decode tasks, longest first
   int32_t* dec_seqs;     // [S] decode sequences in step order
   int64_t* part_base;    // [S] first partial slot of each sequence that is merged
   int32_t* plan_hdr;     // [kHdrSize] counts and the shared prefix, see kHdr*
 };
+
+// One decode task as the planner lists it: one KV partition of a decode row's suffix or
+// of a short multi-row sequence, with what a decode wave needs before its first
+// block-id load, so that a wave's start-up is a chain of two dependent loads (task, then
+// block ids) before it streams keys and values.
+struct DecTask {
+  int32_t seq;        // sequence index
+  int32_t row;        // its first query row (query_start_loc[seq])
+  int32_t nrows;      // its query rows: 1, or 2..16/G
+  int32_t len;        // its tokens (seq_lens[seq])
+  int32_t kbeg, kend; // the task's keys [kbeg, kend)
+  int32_t nparts;     // partitions of the sequence's result, shared-prefix ones first
+  int32_t slot_part;  // this task's partition among them
+};
+static_assert(sizeof(DecTask) == 32, "one 32-byte record per task");
 
 // Partials of a sequence whose decode-path result is split over nparts >= 2 partitions
 // (shared-prefix partitions first, then its own): one slot per (partition, kv head, live

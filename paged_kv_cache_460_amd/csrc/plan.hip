@@ -18,11 +18,11 @@
 //    into partitions like a decode suffix;
 //  * each decode suffix is cut into ceil(len / P) KV partitions of about equal length
 //    (split_parts: whole 32-key steps, at most P). dec_tasks lists every (sequence,
-//    partition) longest first: those of exactly P keys in sequence order, then the others
-//    in 32 length buckets, longest bucket first. Workgroups are dispatched in list
-//    order, so the last ones to start are the shortest and the tail of the decode launch
-//    is short. (The order inside a bucket depends on timing; each task's result does
-//    not.)
+//    partition) as a DecTask record, longest first: those of exactly P keys in sequence
+//    order, then the others in 32 length buckets, longest bucket first. Workgroups are
+//    dispatched in list order, so the last ones to start are the shortest and the tail
+//    of the decode launch is short. (The order inside a bucket depends on timing; each
+//    task's result does not.)
 //
 // One workgroup of 1024 threads: each thread takes a contiguous run of sequences,
 // counts, and after block-wide scans and reductions writes its entries. A recorded step
@@ -120,9 +120,9 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
   __shared__ int32_t bcount[kBuckets];
   __shared__ int32_t bfill[kBuckets];
   __shared__ int32_t boff[kBuckets];
-  // Query rows, lengths and first block id of each sequence, staged once (steps of up
-  // to kLdsSeqs sequences; larger ones read them from memory each time).
-  __shared__ int32_t s_rows[kLdsSeqs], s_len[kLdsSeqs], s_b0[kLdsSeqs];
+  // First query row, query rows, length and first block id of each sequence, staged
+  // once (steps of up to kLdsSeqs sequences; larger ones read them from memory each time).
+  __shared__ int32_t s_q0[kLdsSeqs], s_rows[kLdsSeqs], s_len[kLdsSeqs], s_b0[kLdsSeqs];
   const int32_t* __restrict__ qsl = p.qsl;
   const int32_t* __restrict__ seq_lens = p.seq_lens;
   const int num_seqs = p.num_seqs;
@@ -136,12 +136,14 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
   }
   if (staged) {
     for (int i = tid; i < num_seqs; i += 1024) {
+      s_q0[i] = qsl[i];
       s_rows[i] = qsl[i + 1] - qsl[i];
       s_len[i] = seq_lens[i];
       s_b0[i] = p.block_tables[(int64_t)i * MB];
     }
   }
   lds_barrier();
+  auto q0_of = [&](int i) { return staged ? s_q0[i] : qsl[i]; };
   auto rows_of = [&](int i) { return staged ? s_rows[i] : qsl[i + 1] - qsl[i]; };
   auto len_of = [&](int i) { return staged ? s_len[i] : seq_lens[i]; };
   auto b0_of = [&](int i) { return staged ? s_b0[i] : p.block_tables[(int64_t)i * MB]; };
@@ -335,6 +337,22 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
     const int len = task_len(i);
     const PartSplit sp = split_parts(len, P);
     if (sp.n > 0) {
+      const int n = rows_of(i);
+      const int pre_keys = n == 1 ? prefix_keys : 0;
+      const int pre_parts = n == 1 ? pparts : 0;
+      DecTask task;
+      task.seq = i;
+      task.row = q0_of(i);
+      task.nrows = n;
+      task.len = len_of(i);
+      task.nparts = pre_parts + sp.n;
+      // partition q of the sequence's own range [pre_keys, len) at list position at
+      auto put = [&](int at, int q) {
+        task.kbeg = pre_keys + q * sp.plen;
+        task.kend = min(task.len, task.kbeg + sp.plen);
+        task.slot_part = pre_parts + q;
+        p.dec_tasks[at] = task;
+      };
       const int last = len - (sp.n - 1) * sp.plen;
       if (sp.n > 1) {
         int at;
@@ -345,15 +363,10 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
           const int bk = bucket(sp.plen);
           at = boff[bk] + atomicAdd(&bfill[bk], sp.n - 1);
         }
-        for (int q = 0; q + 1 < sp.n; ++q) {
-          p.dec_tasks[2 * (at + q)] = i;
-          p.dec_tasks[2 * (at + q) + 1] = q;
-        }
+        for (int q = 0; q + 1 < sp.n; ++q) put(at + q, q);
       }
       const int bk = bucket(last);
-      const int at = last == P ? full_run++ : boff[bk] + atomicAdd(&bfill[bk], 1);
-      p.dec_tasks[2 * at] = i;
-      p.dec_tasks[2 * at + 1] = sp.n - 1;
+      put(last == P ? full_run++ : boff[bk] + atomicAdd(&bfill[bk], 1), sp.n - 1);
     }
     p.part_base[i] = unit_run * unit_slots;
     unit_run += part_units(i);
