@@ -327,3 +327,32 @@ def test_shared_prefix_many_decode_rows():
     info = _plan_info(step)
     assert info["decode_rows"] == S and info["shared_prefix_keys"] == 96 and info["shared_prefix_parts"] == 1, info
     assert info["shared_prefix_part_keys"] == 128 and info["partial_slots"] == S * 2 * 1 * 4, info
+
+
+def test_more_sequences_than_the_planner_stages():
+    """2600 sequences, more than the 2048 whose lengths the planner keeps in LDS: it reads
+    them from memory instead. Decode rows, 2..4-row sequences (decode path, G = 4) and
+    chunks, all compared with the oracle, and the task list covering every row."""
+    rng = np.random.default_rng(5)
+    S = 2600
+    qlen = np.ones(S, np.int64)
+    qlen[rng.choice(S, 300, replace=False)] = rng.integers(2, 5, 300)
+    chunk_at = rng.choice(np.nonzero(qlen == 1)[0], 4, replace=False)
+    qlen[chunk_at] = [5, 17, 40, 70]
+    ctx = rng.integers(0, 200, S)
+    step = workload.build_step(ctx, qlen, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", seed=13,
+                               device=DEV, name="unstaged_planner")
+    check_full(step, "unstaged_planner")
+    info = _plan_info(step)
+    assert info["decode_rows"] == int((qlen == 1).sum()), info
+
+
+def test_shared_prefix_more_sequences_than_staged():
+    """2200 decode rows on one shared prefix: the planner compares the block tables with
+    its lengths read from memory, and the prefix is still found and attended once."""
+    S = 2200
+    suffix = [1 + (7 * i) % 33 for i in range(S)]
+    step = _shared_prefix_step(5, suffix, 8, 2, 128)
+    check_full(step, "shared_prefix/unstaged")
+    info = _plan_info(step)
+    assert info["decode_rows"] == S and info["shared_prefix_keys"] == 80 and info["shared_prefix_parts"] == 1, info
