@@ -10,6 +10,8 @@ Then:
 * attention: every row, elementwise within abs 1e-2 / rel 2e-2 plus the per-sequence
   norm bound, with the oracle run on groups of sequences (each group cut out of the
   pre-write pools, so the oracle sees the same inputs and writes the new tokens itself).
+Then the configuration bench.py times: the whole step recorded as one HIP graph and
+replayed twice, every output bit, slot and pool bit equal to the eager results above.
 The GPU result of a workload is kept between the tests that check its groups, and freed
 when the next workload starts.
 """
@@ -142,6 +144,39 @@ def rows_of(step):
 
 # ---------------------------------------------------------------------------------------
 
+def check_graph_replay(name):
+    """The launch configuration bench.py times: the whole step (slot mapping, cache write,
+    attention) recorded once as a HIP graph over the workload's buffers and replayed. Two
+    replays: slots, both pools and every output bit equal to the eager calls' results,
+    which the tests before this one compare with the oracle."""
+    import paged_kv_cache_460_amd as pa
+
+    res = full_run(name)
+    step = res["step"]
+    kc, vc = step.k_cache.clone(), step.v_cache.clone()
+    out = torch.full_like(step.q, float("nan"))
+    slots = torch.empty(step.num_tokens, dtype=torch.int64, device=DEV)
+    ws = torch.empty(pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, step.num_tokens,
+                                                 step.num_q_heads, step.num_kv_heads, step.head_dim, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    graph = pa.StepGraph(step.q, step.k, step.v, kc, vc, step.block_tables, step.seq_lens, step.query_start_loc,
+                         step.context_lens, step.scale, out, slots, ws)
+    try:
+        for r in range(2):
+            log(f"[full] {name}: graph replay {r}")
+            out.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(slots, res["slots"]), f"{name} replay {r}: slot mapping"
+            assert torch.equal(_bits(kc), _bits(res["k_cache"])), f"{name} replay {r}: key cache"
+            assert torch.equal(_bits(vc), _bits(res["v_cache"])), f"{name} replay {r}: value cache"
+            assert torch.equal(_bits(out), _bits(res["out"])), f"{name} replay {r}: attention output"
+    finally:
+        graph.close()
+    del kc, vc, out, ws
+    torch.cuda.empty_cache()
+
+
 def test_full_decode_batch():
     res = full_run("decode_batch_bf16")
     step = res["step"]
@@ -178,6 +213,10 @@ def test_full_decode_batch_wide_tables():
     assert torch.equal(_bits(out_n), _bits(res["out"])), "workspace call differs from the first"
 
 
+def test_full_decode_batch_graph():
+    check_graph_replay("decode_batch_bf16")
+
+
 def test_full_prefix_shared():
     import paged_kv_cache_460_amd as pa
 
@@ -204,6 +243,24 @@ def _decode_partitions(length, P):
     n0 = -(-length // P)
     plen = min(P, -(-(-(-length // n0)) // 32) * 32)
     return -(-length // plen)
+
+
+def test_full_prefix_shared_graph():
+    check_graph_replay("prefix_shared_bf16")
+
+
+def test_full_spec_verify_default_partitions():
+    """The verification step with the partition length the planner chooses (what bench.py
+    times): every row against the oracle."""
+    res = full_run("spec_verify_bf16")
+    step = res["step"]
+    check_indices_and_pool(res, "spec_verify_bf16 (planner P)", oracle_pool=True)
+    n = check_all_groups(res, seq_groups(step, 64 * 1024), "spec_verify_bf16 (planner P)")
+    assert n == rows_of(step) == 256
+
+
+def test_full_spec_verify_graph():
+    check_graph_replay("spec_verify_bf16")
 
 
 def test_full_spec_verify(monkeypatch):
@@ -263,6 +320,11 @@ def test_full_mixed_step_rows_covered():
     assert seen == list(range(step.num_seqs))
 
 
+def test_full_mixed_step_graph():
+    """The mixed step's graph records the prefill kernel on a branch beside decode."""
+    check_graph_replay("mixed_step_bf16")
+
+
 @pytest.mark.parametrize("half", range(2))
 def test_full_long_decode(half):
     res = full_run("long_decode_bf16")
@@ -274,5 +336,8 @@ def test_full_long_decode(half):
     mine = list(range(S))[half * S // 2:(half + 1) * S // 2]
     n = check_all_groups(res, [[i] for i in mine], f"long_decode_bf16 half {half}")
     assert n == len(mine)
-    if half == 1:
-        _CACHE.clear()
+
+
+def test_full_long_decode_graph():
+    check_graph_replay("long_decode_bf16")
+    _CACHE.clear()
