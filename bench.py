@@ -91,6 +91,45 @@ def step_work(step, prefix_keys=0):
             "attn_f32_flops": f32_flops}
 
 
+def clocks_under_load(busy, limit_s=20.0):
+    """rocm-smi's current engine (sclk) and memory (mclk) clocks in MHz, read while `busy`
+    (a batch of eager steps) runs back to back, so that the reading is the clock under this
+    load; None where rocm-smi is missing or fails."""
+    import re
+    import subprocess
+
+    import torch
+
+    try:
+        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    steps = 0
+    while proc.poll() is None and time.perf_counter() - t0 < limit_s:
+        busy()
+        torch.cuda.synchronize()
+        steps += 1
+    try:
+        text, _ = proc.communicate(timeout=5)
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return None
+    try:
+        card = json.loads(text)["card0"]
+    except (ValueError, KeyError, TypeError):
+        return None
+    mhz = {}
+    for key, val in card.items():
+        m = re.match(r"(\w+) clock speed", key)
+        n = re.search(r"(\d+)\s*Mhz", str(val), re.I)
+        if m and n:
+            mhz[f"{m.group(1)}_mhz"] = int(n.group(1))
+    return {**mhz, "batches_run_while_reading": steps} if mhz else None
+
+
 def profiled_traffic(workload_name):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None.
 
@@ -430,6 +469,7 @@ def main():
             "flush_mib": args.flush_mib,
         },
     }
+    result["gpu_clocks"] = clocks_under_load(lambda: [run_step() for _ in range(20)])
     if args.copy_probe_mib > 0:
         n = (args.copy_probe_mib << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
