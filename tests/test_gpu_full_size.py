@@ -234,6 +234,8 @@ def test_full_prefix_shared():
                  step.context_lens, step.scale, out=out, workspace=ws)
     info = pa.attention_plan_info(ws, step.q, res["k_cache"], step.block_tables)
     assert info["decode_rows"] == 128 and info["shared_prefix_keys"] == 4096, info
+    # at most 512 prefix partials per (kv head, column): 4 partitions of 1024 keys
+    assert info["shared_prefix_parts"] == 4 and info["shared_prefix_part_keys"] == 1024, info
     assert torch.equal(_bits(out), _bits(res["out"])), "second call differs from the first"
 
 
