@@ -91,44 +91,6 @@ def step_work(step, prefix_keys=0):
             "attn_f32_flops": f32_flops}
 
 
-def clocks_under_load(busy, samples=7):
-    """The GPU's current engine (gfx) and memory clocks in MHz, read in this process through
-    the amdsmi library while `busy` (a batch of eager steps, enqueued without waiting) runs,
-    so that they are the clocks under this load: medians of `samples` readings. None where
-    the library is missing or does not see exactly one GPU. (No child process: a program
-    started from a process that has initialised the GPU is not allowed to replace itself.)"""
-    import torch
-
-    try:
-        import amdsmi
-    except ImportError:
-        return None
-    try:
-        amdsmi.amdsmi_init()
-    except Exception:  # noqa: BLE001 (any failure of the library means no reading)
-        return None
-    try:
-        handles = amdsmi.amdsmi_get_processor_handles()
-        if len(handles) != 1:
-            return None
-        sclk, mclk = [], []
-        for _ in range(samples):
-            busy()
-            time.sleep(0.002)
-            sclk.append(amdsmi.amdsmi_get_clock_info(handles[0], amdsmi.AmdSmiClkType.GFX)["clk"])
-            mclk.append(amdsmi.amdsmi_get_clock_info(handles[0], amdsmi.AmdSmiClkType.MEM)["clk"])
-            torch.cuda.synchronize()
-        return {"sclk_mhz": float(np.median(sclk)), "mclk_mhz": float(np.median(mclk)), "samples": samples,
-                "source": "amdsmi, in process"}
-    except Exception:  # noqa: BLE001
-        return None
-    finally:
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:  # noqa: BLE001
-            pass
-
-
 def profiled_traffic(workload_name):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None.
 
@@ -468,8 +430,6 @@ def main():
             "flush_mib": args.flush_mib,
         },
     }
-    batch = max(20, int(10.0 / max(eager_ms_per_step, 1e-3)))  # at least 10 ms of work per reading
-    result["gpu_clocks"] = clocks_under_load(lambda: [run_step() for _ in range(batch)])
     if args.copy_probe_mib > 0:
         n = (args.copy_probe_mib << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
