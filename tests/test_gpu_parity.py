@@ -356,3 +356,35 @@ def test_shared_prefix_more_sequences_than_staged():
     check_full(step, "shared_prefix/unstaged")
     info = _plan_info(step)
     assert info["decode_rows"] == S and info["shared_prefix_keys"] == 80 and info["shared_prefix_parts"] == 1, info
+
+
+def _random_case(k):
+    """Seeded random step k: sequence count, query-length mix (empty, decode, 2..16/G-row,
+    chunk), context lengths, GQA group, head dim and dtype all drawn; every fourth bf16 case
+    has its decode rows share a prefix."""
+    rng = np.random.default_rng(1000 + k)
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    dtype = "f32" if k % 6 == 5 else "bf16"
+    S = int(rng.integers(1, 41))
+    kind = rng.choice(4, size=S, p=[0.1, 0.55, 0.15, 0.2])  # empty, decode, multi-row, chunk
+    multi_max = max(2, 16 // G)
+    qlen = np.where(kind == 0, 0, np.where(kind == 1, 1, np.where(
+        kind == 2, rng.integers(2, multi_max + 1, S), rng.integers(multi_max + 1, 300, S))))
+    ctx = rng.integers(0, 600, S)
+    return ctx, qlen, G * hkv, hkv, d, dtype
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_random_steps(k):
+    ctx, qlen, hq, hkv, d, dtype = _random_case(k)
+    if dtype == "bf16" and k % 4 == 0 and (qlen == 1).sum() >= 2:
+        suffix = [1 + int(c) % 40 for c in ctx[qlen == 1]]
+        step = _shared_prefix_step(5, suffix, hq, hkv, d, seed=2000 + k)
+        label = f"random/{k} (shared prefix)"
+    else:
+        step = workload.build_step(ctx, qlen, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                                   seed=2000 + k, device=DEV, name=f"random_{k}")
+        label = f"random/{k}"
+    check_full(step, label)
