@@ -33,6 +33,7 @@
 namespace pa {
 
 namespace {
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBuckets = 32;
 constexpr int kMinPrefixBlocks = 4;  // shorter shared runs are left to the decode kernel
 constexpr int kLdsSeqs = 2048;       // sequences whose lengths the planner stages in LDS
@@ -203,36 +204,65 @@ __device__ void plan_block(const AttnParams& p, int32_t rows_per_tile) {
   int prefix_blocks = 0;
   const int cap = mins[1];
   if (total_dec >= 2 && mins[2] == -mins[3] && cap >= kMinPrefixBlocks) {
-    const int32_t* __restrict__ bref = p.block_tables + mins[0] * MB;
-    // Wave w compares sequences w, w + 16, ... four at a time, its lanes over the
-    // blocks, four blocks per lane at a time; each lane keeps the first mismatching block
-    // it saw. The comparisons are selects, not branches, so all 20 loads of a round are
-    // in flight together. (Indices past the run are clamped to its last block: every
-    // table row holds MB >= cap entries.)
+    const int32_t* __restrict__ bref = p.block_tables + (int64_t)mins[0] * MB;
+    // Each lane keeps the first mismatching block it saw. The comparisons are selects, not
+    // branches, so all loads of a round are in flight together.
     const int lane = tid & 63, w = tid >> 6;
     int bad = cap;
-    for (int i0 = w; i0 < num_seqs; i0 += 4 * 16) {
-      bool dec[4];
-      const int32_t* __restrict__ row[4];
+    // Rows of 16-byte-aligned tables (aligned base, width a multiple of 4) are compared
+    // four blocks per 16-byte load: wave w takes sequences w, w + 16, ... eight at a time,
+    // lane l blocks c0 + 4l .. c0 + 4l + 3 of each (c0 + 4l < cap <= MB, and both are
+    // multiples of 4, so all four lie in the row); blocks past the run are not counted.
+    const bool vec = MB % 4 == 0 && (reinterpret_cast<uintptr_t>(p.block_tables) & 15) == 0;
+    if (vec) {
+      for (int i0 = w; i0 < num_seqs; i0 += 8 * 16) {
+        bool dec[8];
+        const int32_t* __restrict__ row[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = min(i0 + 16 * u, num_seqs - 1);
-        dec[u] = i0 + 16 * u < num_seqs && rows_of(i) == 1;
-        row[u] = p.block_tables + (int64_t)i * MB;
-      }
-      for (int c0 = lane; c0 < cap; c0 += 4 * 64) {
-        int r[4], x[4][4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int cc = min(c0 + 64 * v, cap - 1);
-          r[v] = bref[cc];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) x[u][v] = row[u][cc];
+        for (int u = 0; u < 8; ++u) {
+          const int i = min(i0 + 16 * u, num_seqs - 1);
+          dec[u] = i0 + 16 * u < num_seqs && rows_of(i) == 1;
+          row[u] = p.block_tables + (int64_t)i * MB;
         }
+        for (int c0 = 4 * lane; c0 < cap; c0 += 4 * 64) {
+          const i32x4 r = *reinterpret_cast<const i32x4*>(bref + c0);
+          i32x4 x[8];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+          for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const i32x4*>(row[u] + c0);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) bad = (dec[u] && x[u][v] != r[v]) ? min(bad, c0 + 64 * v) : bad;
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              bad = (c0 + e < cap && dec[u] && x[u][e] != r[e]) ? min(bad, c0 + e) : bad;
+        }
+      }
+    } else {
+      // Otherwise four sequences at a time, each lane four blocks 64 apart per round.
+      // (Indices past the run are clamped to its last block: every table row holds
+      // MB >= cap entries.)
+      for (int i0 = w; i0 < num_seqs; i0 += 4 * 16) {
+        bool dec[4];
+        const int32_t* __restrict__ row[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = min(i0 + 16 * u, num_seqs - 1);
+          dec[u] = i0 + 16 * u < num_seqs && rows_of(i) == 1;
+          row[u] = p.block_tables + (int64_t)i * MB;
+        }
+        for (int c0 = lane; c0 < cap; c0 += 4 * 64) {
+          int r[4], x[4][4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int cc = min(c0 + 64 * v, cap - 1);
+            r[v] = bref[cc];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u][v] = row[u][cc];
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) bad = (dec[u] && x[u][v] != r[v]) ? min(bad, c0 + 64 * v) : bad;
+        }
       }
     }
     int32_t m[1] = {bad};

@@ -175,14 +175,20 @@ def test_shared_prefix_equals_private_copies():
     assert_attention_close(to_f64(a), to_f64(b), qsl, "bf16", label="shared vs private")
 
 
-def _shared_prefix_step(prefix_blocks, suffix_lens, hq, hkv, d, chunks=(), seed=21, unshared=False, diverge=None):
+def _shared_prefix_step(prefix_blocks, suffix_lens, hq, hkv, d, chunks=(), seed=21, unshared=False, diverge=None,
+                        width="natural"):
     """Decode sequences that all list the same `prefix_blocks` blocks first (plus optional
     prefill chunks that do not share them). `diverge` = (sequence, block): that sequence
-    shares only the blocks before `block` and keeps its own blocks from there on."""
+    shares only the blocks before `block` and keeps its own blocks from there on.
+    `width`: the block-table width the lengths need ("natural"), rounded up to a multiple of
+    4 ("vec": the planner compares rows with 16-byte loads), or to one more than that
+    ("scalar": one block id per load)."""
     ctx = [prefix_blocks * 16 + s - 1 for s in suffix_lens] + [c for c, _ in chunks]
     qlen = [1] * len(suffix_lens) + [n for _, n in chunks]
+    need = max((c + n + 15) // 16 for c, n in zip(ctx, qlen))
+    mb = {"natural": None, "vec": -(-need // 4) * 4, "scalar": -(-need // 4) * 4 + 1}[width]
     step = workload.build_step(ctx, qlen, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype="bf16", seed=seed,
-                               device=DEV, name="shared_prefix")
+                               max_blocks_per_seq=mb, device=DEV, name="shared_prefix")
     bt = step.block_tables.clone()
     S_dec = len(suffix_lens)
     shared = bt[0, :prefix_blocks].clone()
@@ -236,16 +242,19 @@ SHARED_PREFIX_CASES = {
 }
 
 
+@pytest.mark.parametrize("width", ["vec", "scalar"])
 @pytest.mark.parametrize("case", sorted(SHARED_PREFIX_CASES))
-def test_shared_prefix_cases(case):
+def test_shared_prefix_cases(case, width):
     """Steps whose decode sequences share leading blocks: checked whole against the oracle,
-    and the planner must have found exactly the shared run (or none)."""
+    and the planner must have found exactly the shared run (or none), with tables whose
+    rows it compares four block ids per load and with tables it compares one at a time."""
     import paged_kv_cache_460_amd as pa
 
     nb, suf, hq, hkv, d, chunks, unshared, *rest = SHARED_PREFIX_CASES[case]
     diverge = rest[0] if rest else None
-    step = _shared_prefix_step(nb, suf, hq, hkv, d, chunks=chunks, unshared=unshared, diverge=diverge)
-    check_full(step, f"shared_prefix/{case}")
+    step = _shared_prefix_step(nb, suf, hq, hkv, d, chunks=chunks, unshared=unshared, diverge=diverge, width=width)
+    assert (step.max_blocks_per_seq % 4 == 0) == (width == "vec")
+    check_full(step, f"shared_prefix/{case}/{width}")
     # the same step again with a workspace we keep, to read the plan back
     kc, vc = step.k_cache.clone(), step.v_cache.clone()
     ws = torch.empty(pa.attention_workspace_size(step.num_seqs, step.max_blocks_per_seq, step.num_tokens, hq, hkv, d,
